@@ -1,0 +1,129 @@
+/*
+ * fg.h -- FP8 (OCP E4M3) GEMM with fine-grained fp32 block scales, for AMD
+ * MI355X (gfx950). C ABI.
+ *
+ * Every GEMM entry point computes D = A . B^T with
+ *
+ *     D[m, n] = sum_kb  sa[m, kb] * sb[n / 128, kb] * P_kb[m, n]
+ *     P_kb[m, n] = sum_{k in K-block kb} e4m3(A[m, k]) * e4m3(B[n, k])
+ *
+ * i.e. A is scaled per 1x128 block (one fp32 per row and 128-wide K-block) and
+ * B per 128x128 block, each 128-wide K-block partial is formed in a fresh FP32
+ * accumulator on the matrix cores and then multiplied by sa*sb and added into
+ * a master FP32 accumulator ("two-level accumulation"), and the result is
+ * rounded once to bf16 (round to nearest even).
+ *
+ * Sources: the zwzgs.cn page "DeepGEMM: an open-source FP8 GEMM library",
+ * sections "Features > fine-grained scaling" (DeepSeek-V3 style per-block
+ * scales), "Features > layouts" (normal, MoE contiguous, MoE masked) and
+ * "Technical details > two-level accumulation"; the 2kiu.com DeepGEMM
+ * explainer, section 3.3 (FP8 inputs, FP32 accumulation, conversion to the
+ * output type at the end). The 1x128 / 128x128 granularity and the E4M3
+ * variant (bias 7, max 448, NaN = S.1111.111, no infinities) are the readings
+ * taken where the pages only say "fine-grained" and "E4M3".
+ *
+ * Conventions shared by all calls
+ *   - All pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no device memory and keeps no reference after returning.
+ *   - A, B: E4M3 bytes, K contiguous ("NT": B is given as N x K).
+ *   - sa: fp32, K-block-major: sa[kb * M + m] (masked: [G][K/128][M_max]).
+ *   - sb: fp32, row-major [N/128][K/128] (grouped: [G][N/128][K/128]).
+ *   - D: bf16 bit patterns, row-major [M][N] (masked: [G][M_max][N]).
+ *   - K and N must be multiples of 128; M is arbitrary (>= 0).
+ *   - A, B and D base pointers must be 16-byte aligned, sa and sb 4-byte.
+ *   - Calls are asynchronous on `stream` (0 = null stream), never synchronise
+ *     and never read device data on the host, so they can be captured in a
+ *     HIP graph. Rows the call has no output for are never written.
+ *   - A fixed device, shape and tile configuration gives bitwise identical
+ *     results on every call (no atomics, no split-K).
+ *   - Return value: FG_OK or a negative FG_E* code; no exception crosses the
+ *     ABI. fg_strerror() gives a static description.
+ */
+#ifndef FG_H
+#define FG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FG_OK = 0,
+  FG_EINVAL = -1,        /* bad argument: null pointer, negative size,
+                            K or N not a multiple of 128, misalignment,
+                            G < 1 for a grouped call, unknown tile */
+  FG_EUNSUPPORTED = -2,  /* current device is not gfx950 */
+  FG_ELAUNCH = -3,       /* the kernel launch failed (hipGetLastError) */
+  FG_EDEVICE = -4        /* a HIP runtime query failed */
+};
+
+enum { FG_LAYOUT_DENSE = 0, FG_LAYOUT_CONTIGUOUS = 1, FG_LAYOUT_MASKED = 2 };
+
+/*
+ * Dense ("normal") layout. zwzgs.cn DeepGEMM page, "Features > layouts".
+ *   A  [M][K] E4M3, sa [K/128][M] fp32, B [N][K] E4M3, sb [N/128][K/128] fp32,
+ *   D  [M][N] bf16 (written in full).
+ * M == 0 (or N == 0) returns FG_OK without launching anything.
+ */
+int fg_gemm_fp8_nt(const void* A, const float* sa, const void* B, const float* sb,
+                   void* D, int M, int N, int K, hipStream_t stream);
+
+/*
+ * MoE grouped, contiguous layout (training / prefill). zwzgs.cn DeepGEMM
+ * page, "Features > layouts" and "Applications > MoE".
+ *   A  [M][K] E4M3: the rows of all G experts concatenated along M,
+ *   sa [K/128][M], B [G][N][K] E4M3 (one weight per expert),
+ *   sb [G][N/128][K/128], D [M][N] bf16,
+ *   m_indices [M] int32 (device): expert id of each row, or -1 for a padding
+ *   row. Every aligned 128-row block of A must hold rows of at most one expert
+ *   (plus padding rows); experts' segments are therefore padded to multiples
+ *   of 128 rows. Rows with m_indices = -1 are not written. Ids >= G are
+ *   treated as padding (never read out of bounds).
+ */
+int fg_grouped_contiguous(const void* A, const float* sa, const void* B, const float* sb,
+                          void* D, const int32_t* m_indices, int M, int N, int K, int G,
+                          hipStream_t stream);
+
+/*
+ * MoE grouped, masked layout (decode). zwzgs.cn DeepGEMM page, "Features >
+ * layouts" and "Applications > MoE".
+ *   A  [G][M_max][K] E4M3, sa [G][K/128][M_max], B [G][N][K] E4M3,
+ *   sb [G][N/128][K/128], D [G][M_max][N] bf16,
+ *   masked_m [G] int32 (device): number of valid rows of each expert, clamped
+ *   to [0, M_max] by the kernel. Only rows r < masked_m[g] of expert g are
+ *   written; the rest of D keeps its prior content. masked_m is read only by
+ *   the kernel (no host synchronisation).
+ */
+int fg_grouped_masked(const void* A, const float* sa, const void* B, const float* sb,
+                      void* D, const int32_t* masked_m, int G, int M_max, int N, int K,
+                      hipStream_t stream);
+
+/*
+ * Tile configuration the library would launch for a problem, computed on the
+ * host from sizes only (no device access, usable without a GPU). Tiles are
+ * chosen from a fixed table to minimise wave quantisation over `num_cus`
+ * compute units, the point the zwzgs.cn DeepGEMM page makes in "Technical
+ * details > non-standard block sizes" (M=256, N=7168 on 132 SMs: 112 tiles of
+ * 128x128 versus 128 of 128x112).
+ *   layout  FG_LAYOUT_*; M = total rows (dense, contiguous) or M_max (masked);
+ *   G = experts (1 for dense). num_cus <= 0 means the library's default (256).
+ * Writes the tile's rows/cols to *bm / *bn and the number of workgroups the
+ * launch would use to *grid (any of the three may be NULL).
+ */
+int fg_select_config(int layout, int M, int N, int K, int G, int num_cus,
+                     int* bm, int* bn, int* grid);
+
+/* Force a tile configuration for subsequent calls (bm x bn must be one of the
+ * compiled tiles), or restore automatic selection with bm = bn = 0. Intended
+ * for tests and tile sweeps; process-wide, not thread-safe. */
+int fg_force_tile(int bm, int bn);
+
+/* Static, human-readable description of a return code. */
+const char* fg_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FG_H */

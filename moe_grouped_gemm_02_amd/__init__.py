@@ -1,0 +1,166 @@
+"""FP8 (OCP E4M3) block-scaled GEMM for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libfg.so`` (see ``include/fg.h``):
+argument checking and marshalling only. Every step of the computation runs in
+the library's HIP kernels; there is no CPU or PyTorch fallback, and calls fail
+loudly when the library is missing or the device is not gfx950.
+
+torch is used for device memory and the current HIP stream only.
+
+    D = A . B^T,  D[m, n] = sum_kb sa[m, kb] sb[n // 128, kb] sum_{k in kb} a[m, k] b[n, k]
+
+Tensor conventions (all on the same CUDA/HIP device, contiguous):
+    A   uint8 or float8_e4m3fn  [M, K]        (masked: [G, M_max, K])
+    sa  float32                 [K/128, M]    (masked: [G, K/128, M_max])
+    B   uint8 or float8_e4m3fn  [N, K]        (grouped: [G, N, K])
+    sb  float32                 [N/128, K/128] (grouped: [G, N/128, K/128])
+    D   bfloat16                [M, N]        (masked: [G, M_max, N])
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfg.so")
+
+LAYOUT_DENSE, LAYOUT_CONTIGUOUS, LAYOUT_MASKED = 0, 1, 2
+
+_lib = None
+
+
+class FGError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libfg.so (built in-tree by ``moe_grouped_gemm_02_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m moe_grouped_gemm_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, fp, ip, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+        L.fg_gemm_fp8_nt.argtypes = [vp, fp, vp, fp, vp, i, i, i, vp]
+        L.fg_grouped_contiguous.argtypes = [vp, fp, vp, fp, vp, ip, i, i, i, i, vp]
+        L.fg_grouped_masked.argtypes = [vp, fp, vp, fp, vp, ip, i, i, i, i, vp]
+        L.fg_select_config.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
+                                       ctypes.POINTER(i)]
+        L.fg_force_tile.argtypes = [i, i]
+        L.fg_strerror.argtypes = [i]
+        L.fg_strerror.restype = ctypes.c_char_p
+        for name in ("fg_gemm_fp8_nt", "fg_grouped_contiguous", "fg_grouped_masked",
+                     "fg_select_config", "fg_force_tile"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code):
+    return lib().fg_strerror(int(code)).decode()
+
+
+def _check(code, what):
+    if code != 0:
+        raise FGError(f"{what}: {strerror(code)} (code {code})")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _fp8(t, name, shape):
+    torch = _torch()
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"{name} must be uint8 or float8_e4m3fn E4M3 bytes, got {t.dtype}")
+    _dev(t, name, shape)
+
+
+def _dev(t, name, shape, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def gemm_fp8_nt(A, sa, B, sb, D):
+    """Dense D[M, N] = A[M, K] . B[N, K]^T with block scales; writes D in place."""
+    torch = _torch()
+    M, K = A.shape
+    N = B.shape[0]
+    _fp8(A, "A", (M, K))
+    _fp8(B, "B", (N, K))
+    if K % 128 or N % 128:
+        raise ValueError("K and N must be multiples of 128")
+    _dev(sa, "sa", (K // 128, M), torch.float32)
+    _dev(sb, "sb", (N // 128, K // 128), torch.float32)
+    _dev(D, "D", (M, N), torch.bfloat16)
+    _check(lib().fg_gemm_fp8_nt(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D), M, N, K,
+                                _stream(A)), "fg_gemm_fp8_nt")
+    return D
+
+
+def grouped_contiguous(A, sa, B, sb, D, m_indices):
+    """MoE contiguous layout: rows of A belong to expert m_indices[row] (-1 = padding,
+    not written); B is [G, N, K]."""
+    torch = _torch()
+    M, K = A.shape
+    G, N = B.shape[0], B.shape[1]
+    _fp8(A, "A", (M, K))
+    _fp8(B, "B", (G, N, K))
+    if K % 128 or N % 128:
+        raise ValueError("K and N must be multiples of 128")
+    _dev(sa, "sa", (K // 128, M), torch.float32)
+    _dev(sb, "sb", (G, N // 128, K // 128), torch.float32)
+    _dev(D, "D", (M, N), torch.bfloat16)
+    _dev(m_indices, "m_indices", (M,), torch.int32)
+    _check(lib().fg_grouped_contiguous(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D),
+                                       _ptr(m_indices), M, N, K, G, _stream(A)),
+           "fg_grouped_contiguous")
+    return D
+
+
+def grouped_masked(A, sa, B, sb, D, masked_m):
+    """MoE masked layout: expert g has masked_m[g] valid rows of A[g]; only those rows
+    of D[g] are written. masked_m stays on the device."""
+    torch = _torch()
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    _fp8(A, "A", (G, M_max, K))
+    _fp8(B, "B", (G, N, K))
+    if K % 128 or N % 128:
+        raise ValueError("K and N must be multiples of 128")
+    _dev(sa, "sa", (G, K // 128, M_max), torch.float32)
+    _dev(sb, "sb", (G, N // 128, K // 128), torch.float32)
+    _dev(D, "D", (G, M_max, N), torch.bfloat16)
+    _dev(masked_m, "masked_m", (G,), torch.int32)
+    _check(lib().fg_grouped_masked(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D),
+                                   _ptr(masked_m), G, M_max, N, K, _stream(A)),
+           "fg_grouped_masked")
+    return D
+
+
+def select_config(layout, M, N, K, G=1, num_cus=0):
+    """(bm, bn, grid) the library would launch; host-only, no device access."""
+    bm, bn, grid = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().fg_select_config(layout, M, N, K, G, num_cus, ctypes.byref(bm),
+                                  ctypes.byref(bn), ctypes.byref(grid)), "fg_select_config")
+    return bm.value, bn.value, grid.value
+
+
+def force_tile(bm=0, bn=0):
+    """Force a compiled tile shape for later calls; (0, 0) restores automatic choice."""
+    _check(lib().fg_force_tile(bm, bn), "fg_force_tile")

@@ -1,0 +1,48 @@
+"""Ahead-of-time build of the HIP library (libfg.so) for gfx950.
+
+Run ``python -m moe_grouped_gemm_02_amd.build`` (or call ``build()``). The
+shared object is written next to this file so that it travels with the source
+tree; nothing is installed elsewhere.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libfg.so")
+SOURCES = ["fg_host.hip"]
+HEADERS = ["fg_kernel.hpp"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # packed fp32 VALU forms stay off: plain v_fma_f32 only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into VGPRs: the promotion FMA reads them there
+    # (an AGPR destination would cost one v_accvgpr_read per element)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def build(verbose=False):
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libfg.so")
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,208 @@
+// fg_host.hip -- host side of the FP8 block-scaled GEMM library: argument
+// validation, device checks, tile selection and kernel launch behind the C ABI
+// declared in include/fg.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "fg.h"
+#include "fg_kernel.hpp"
+
+namespace {
+
+using fg::Params;
+
+// ---------------------------------------------------------------- devices
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+// Checks that the current device is gfx950; caches its CU count.
+int current_device(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FG_EDEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return FG_EDEVICE;
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FG_EDEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    st = ok ? 1 : -1;
+    g_dev_state[dev].store(st, std::memory_order_release);
+  }
+  if (st < 0) return FG_EUNSUPPORTED;
+  if (cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return FG_OK;
+}
+
+// ---------------------------------------------------------------- tiles
+struct Tile {
+  int bm, bn;
+};
+// Compiled tile shapes (rows x cols of D per workgroup).
+constexpr Tile kTiles[] = {{128, 128}};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+constexpr int kDefaultCUs = 256;
+
+std::atomic<int> g_forced_tile{-1};
+
+inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+// Number of tiles a problem splits into with a given tile shape.
+long count_tiles(int layout, int M, int N, int G, const Tile& t) {
+  const long tn = ceil_div(N, t.bn);
+  if (layout == FG_LAYOUT_MASKED) return (long)G * ceil_div(M, t.bm) * tn;
+  return (long)ceil_div(M, t.bm) * tn;
+}
+
+// Picks the tile index for a problem: among the compiled tiles, the one whose
+// tile count fills the CUs best (fraction of busy CU-slots over all waves),
+// preferring larger tiles on ties.
+int pick_tile(int layout, int M, int N, int G, int cus) {
+  const int forced = g_forced_tile.load(std::memory_order_relaxed);
+  if (forced >= 0) return forced;
+  int best = 0;
+  double best_eff = -1.0;
+  for (int i = 0; i < kNumTiles; ++i) {
+    if (layout == FG_LAYOUT_CONTIGUOUS && 128 % kTiles[i].bm != 0) continue;
+    const long tiles = count_tiles(layout, M, N, G, kTiles[i]);
+    const long waves = (tiles + cus - 1) / cus;
+    const double eff = waves ? (double)tiles / (double)(waves * cus) : 0.0;
+    const double area = (double)kTiles[i].bm * kTiles[i].bn;
+    const double best_area = (double)kTiles[best].bm * kTiles[best].bn;
+    if (eff > best_eff + 1e-9 || (eff > best_eff - 1e-9 && area > best_area)) {
+      best = i;
+      best_eff = eff;
+    }
+  }
+  return best;
+}
+
+template <int LAYOUT>
+hipError_t launch_layout(int tile, const Params& p, int grid, hipStream_t s) {
+  switch (tile) {
+    case 0:
+      hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, 128, 128>), dim3(grid), dim3(fg::kThreads), 0, s, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int run(int layout, const void* A, const float* sa, const void* B, const float* sb, void* D,
+        const int32_t* m_indices, const int32_t* masked_m, int M, int N, int K, int G,
+        hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 128 || (K % 128) != 0 || (N % 128) != 0) return FG_EINVAL;
+  if (layout != FG_LAYOUT_DENSE && G < 1) return FG_EINVAL;
+  if (M == 0 || N == 0) return FG_OK;
+  if (!A || !sa || !B || !sb || !D) return FG_EINVAL;
+  if (layout == FG_LAYOUT_CONTIGUOUS && !m_indices) return FG_EINVAL;
+  if (layout == FG_LAYOUT_MASKED && !masked_m) return FG_EINVAL;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || !aligned(sa, 4) || !aligned(sb, 4))
+    return FG_EINVAL;
+  if (m_indices && !aligned(m_indices, 4)) return FG_EINVAL;
+  if (masked_m && !aligned(masked_m, 4)) return FG_EINVAL;
+
+  int cus = 0;
+  const int st = current_device(&cus);
+  if (st != FG_OK) return st;
+
+  const int ti = pick_tile(layout, M, N, G, cus);
+  const Tile& t = kTiles[ti];
+  // contiguous tiles must not straddle an aligned 128-row expert block
+  if (layout == FG_LAYOUT_CONTIGUOUS && 128 % t.bm != 0) return FG_EINVAL;
+  Params p;
+  p.A = static_cast<const uint8_t*>(A);
+  p.sa = sa;
+  p.B = static_cast<const uint8_t*>(B);
+  p.sb = sb;
+  p.D = static_cast<uint16_t*>(D);
+  p.m_indices = m_indices;
+  p.masked_m = masked_m;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.G = layout == FG_LAYOUT_DENSE ? 1 : G;
+  p.KB = K / 128;
+  p.tiles_m = ceil_div(M, t.bm);
+  p.tiles_n = ceil_div(N, t.bn);
+  const long tiles = count_tiles(layout, M, N, p.G, t);
+  if (tiles > 0x7fffffffL) return FG_EINVAL;
+  const int grid = (int)tiles;
+
+  hipError_t e;
+  switch (layout) {
+    case FG_LAYOUT_DENSE: e = launch_layout<fg::kDense>(ti, p, grid, stream); break;
+    case FG_LAYOUT_CONTIGUOUS: e = launch_layout<fg::kContiguous>(ti, p, grid, stream); break;
+    default: e = launch_layout<fg::kMasked>(ti, p, grid, stream); break;
+  }
+  return e == hipSuccess ? FG_OK : FG_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fg_gemm_fp8_nt(const void* A, const float* sa, const void* B, const float* sb, void* D,
+                   int M, int N, int K, hipStream_t stream) {
+  return run(FG_LAYOUT_DENSE, A, sa, B, sb, D, nullptr, nullptr, M, N, K, 1, stream);
+}
+
+int fg_grouped_contiguous(const void* A, const float* sa, const void* B, const float* sb,
+                          void* D, const int32_t* m_indices, int M, int N, int K, int G,
+                          hipStream_t stream) {
+  return run(FG_LAYOUT_CONTIGUOUS, A, sa, B, sb, D, m_indices, nullptr, M, N, K, G, stream);
+}
+
+int fg_grouped_masked(const void* A, const float* sa, const void* B, const float* sb,
+                      void* D, const int32_t* masked_m, int G, int M_max, int N, int K,
+                      hipStream_t stream) {
+  if (G < 1) return FG_EINVAL;
+  return run(FG_LAYOUT_MASKED, A, sa, B, sb, D, nullptr, masked_m, M_max, N, K, G, stream);
+}
+
+int fg_select_config(int layout, int M, int N, int K, int G, int num_cus, int* bm, int* bn,
+                     int* grid) {
+  if (layout < FG_LAYOUT_DENSE || layout > FG_LAYOUT_MASKED) return FG_EINVAL;
+  if (M < 0 || N < 0 || K < 0 || (layout != FG_LAYOUT_DENSE && G < 1)) return FG_EINVAL;
+  if (layout == FG_LAYOUT_DENSE) G = 1;
+  const int cus = num_cus > 0 ? num_cus : kDefaultCUs;
+  const int ti = pick_tile(layout, M, N, G, cus);
+  if (bm) *bm = kTiles[ti].bm;
+  if (bn) *bn = kTiles[ti].bn;
+  if (grid) *grid = (int)count_tiles(layout, M, N, G, kTiles[ti]);
+  return FG_OK;
+}
+
+int fg_force_tile(int bm, int bn) {
+  if (bm == 0 && bn == 0) {
+    g_forced_tile.store(-1);
+    return FG_OK;
+  }
+  for (int i = 0; i < kNumTiles; ++i) {
+    if (kTiles[i].bm == bm && kTiles[i].bn == bn) {
+      g_forced_tile.store(i);
+      return FG_OK;
+    }
+  }
+  return FG_EINVAL;
+}
+
+const char* fg_strerror(int code) {
+  switch (code) {
+    case FG_OK: return "success";
+    case FG_EINVAL: return "invalid argument (null pointer, negative size, K or N not a multiple of 128, K < 128, misaligned pointer, G < 1 or unknown tile)";
+    case FG_EUNSUPPORTED: return "unsupported device (gfx950 required)";
+    case FG_ELAUNCH: return "kernel launch failed";
+    case FG_EDEVICE: return "HIP device query failed";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

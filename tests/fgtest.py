@@ -1,0 +1,73 @@
+"""Shared helpers for the GPU parity tests: seeded inputs quantised by the
+oracle on the CPU, marshalled into the library's layouts, and results brought
+back for the oracle's check. Nothing here computes the GEMM."""
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+SENTINEL = 0x7E7E          # bf16 bits of a finite value no GEMM here produces by chance
+
+
+def dev():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a HIP device")
+    return torch.device("cuda", 0)
+
+
+def to_dev(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(dev())
+
+
+def d_bits(D):
+    return D.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def new_out(shape, prefill_bits=SENTINEL):
+    D = torch.empty(shape, dtype=torch.bfloat16, device=dev())
+    D.view(torch.int16).fill_(np.int16(np.uint16(prefill_bits).view(np.int16)))
+    return D
+
+
+def quant_dense(a, b):
+    """fp32 A [M,K], B [N,K] -> oracle codes/scales in natural layout."""
+    A, sa = oracle.quantize_act_1x128(a)
+    B, sb = oracle.quantize_weight_128x128(b)
+    return A, sa, B, sb
+
+
+def dense_inputs(A, sa, B, sb):
+    """Natural-layout codes/scales -> device tensors in the ABI layout
+    (sa transposed to K-block-major)."""
+    return (to_dev(A), to_dev(np.ascontiguousarray(sa.T)), to_dev(B), to_dev(sb))
+
+
+def masked_inputs(A, sa, B, sb):
+    return (to_dev(A), to_dev(np.ascontiguousarray(np.transpose(sa, (0, 2, 1)))), to_dev(B), to_dev(sb))
+
+
+def make_dense(M, N, K, seed, **kw):
+    w = workloads.dense(M, N, K, seed, **kw)
+    return quant_dense(w["a"], w["b"])
+
+
+def make_contiguous(G, N, K, seed, **kw):
+    w = workloads.contiguous(G, N, K, seed, **kw)
+    A, sa = oracle.quantize_act_1x128(w["a"])
+    B, sb = oracle.quantize_weight_128x128(w["b"])
+    return A, sa, B, sb, w["m_indices"]
+
+
+def make_masked(G, M_max, N, K, seed, **kw):
+    w = workloads.masked(G, M_max, N, K, seed, **kw)
+    Gs = w["a"].shape[0]
+    A = np.empty(w["a"].shape, np.uint8)
+    sa = np.empty((Gs, M_max, K // 128), np.float32)
+    for g in range(Gs):
+        A[g], sa[g] = oracle.quantize_act_1x128(w["a"][g])
+    B, sb = oracle.quantize_weight_128x128(w["b"])
+    return A, sa, B, sb, w["masked_m"]
