@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Throughput of the FP8 (E4M3) block-scaled GEMM on one MI355X.
+
+One step = one library call (host validation + tile choice, then the kernel:
+tile scheduling, staging, E4M3 MFMA per 128-wide K-block, promotion with
+sa*sb into the FP32 master accumulator, bf16 epilogue) over one batch of
+seeded synthetic input that is already resident in device memory.
+
+Headline workload: dense D = A . B^T with M=256, N=7168, K=7168, A and B drawn
+N(0,1) (1% of A's rows scaled x50), quantised on the GPU to E4M3 with fp32
+scales per 1x128 (A) and 128x128 (B) block, bf16 output.
+
+The inputs are replicated into enough copies to exceed the 256 MB last-level
+(MALL) cache, and consecutive steps rotate through the copies, so each launch
+streams its operands from HBM instead of re-reading a cached copy.
+
+Prints ONE JSON line. `value` is TFLOP/s of useful work (2*M*N*K over rows that
+have an output) per wall-clock second over the timed steps. `roofline` is for
+the GEMM kernel, from HIP events recorded on the launch stream around the timed
+steps. `cpu_baseline` is the CPU oracle (dequantise + fp64 GEMM) timed on this
+host. `per_workload` repeats the measurement for the other workloads (the small
+dense case, MoE contiguous, MoE masked, the large dense FFN GEMM) unless
+--headline-only is given.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 256 * 2.4e9 * 8192 / 1e12    # 5033: 256 CUs x 2.4 GHz x 8192 FLOP/clk/CU
+PEAK_HBM_GBPS = 8000.0                          # HBM3E, 8 TB/s
+MALL_BYTES = 256 << 20
+HEADLINE = "dense_skinny"
+ORDER = ["dense_small", "dense_skinny", "contiguous", "masked", "dense_ffn"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline workload (for profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time for the oracle baseline sample")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------- inputs
+def gpu_operands(name, fg, torch):
+    """Seeded fp32 inputs (numpy) -> device -> E4M3 + scales by the library's
+    quantisers. Returns a dict of device tensors and the sizes."""
+    import numpy as np
+    import workloads
+
+    w = workloads.make(name)
+    dev = torch.device("cuda", 0)
+    a = torch.from_numpy(w["a"]).to(dev)
+    b = torch.from_numpy(w["b"]).to(dev)
+    A, sa = fg.quant_act_1x128(a)
+    B, sb = fg.quant_weight_128x128(b)
+    del a, b
+    op = dict(kind=w["kind"], A=A, sa=sa, B=B, sb=sb)
+    N, K = w["b"].shape[-2], w["b"].shape[-1]
+    op.update(N=N, K=K, flop=workloads.useful_flop(w))
+    if w["kind"] == "dense":
+        M = w["a"].shape[0]
+        op.update(M=M, G=1, rows_out=M)
+        op["D"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    elif w["kind"] == "contiguous":
+        M = w["a"].shape[0]
+        op.update(M=M, G=w["b"].shape[0], rows_out=int((w["m_indices"] >= 0).sum()))
+        op["m_indices"] = torch.from_numpy(w["m_indices"]).to(dev)
+        op["D"] = torch.zeros((M, N), dtype=torch.bfloat16, device=dev)
+        op["group_m"] = w["group_m"].tolist()
+    else:
+        G, M_max = w["a"].shape[0], w["a"].shape[1]
+        mm = np.clip(w["masked_m"], 0, M_max)
+        op.update(M=M_max, G=G, rows_out=int(mm.sum()))
+        op["masked_m"] = torch.from_numpy(w["masked_m"]).to(dev)
+        op["D"] = torch.zeros((G, M_max, N), dtype=torch.bfloat16, device=dev)
+        op["masked_m_list"] = w["masked_m"].tolist()
+    torch.cuda.synchronize()
+    return op
+
+
+def algorithmic_bytes(op):
+    """Operands read once + output written once, counting only experts and rows
+    that have an output (A rows with work, B of experts with work, their scales,
+    D rows written)."""
+    N, K = op["N"], op["K"]
+    KB = K // 128
+    rows = op["rows_out"]
+    if op["kind"] == "masked":
+        experts = sum(1 for m in op["masked_m_list"] if m > 0)
+    else:
+        experts = op["G"]
+    a = rows * K + rows * KB * 4
+    b = experts * (N * K + (N // 128) * KB * 4)
+    d = rows * N * 2
+    return a + b + d
+
+
+def replicate(op, torch):
+    """Copies of the operands so that consecutive steps do not hit the MALL."""
+    keys = ["A", "sa", "B", "sb"]
+    foot = sum(op[k].numel() * op[k].element_size() for k in keys)
+    n = max(1, min(16, math.ceil(2 * MALL_BYTES / max(foot, 1))))
+    copies = [{k: op[k] for k in keys}]
+    for _ in range(n - 1):
+        copies.append({k: op[k].clone() for k in keys})
+    torch.cuda.synchronize()
+    return copies
+
+
+def make_step(op, copies, fg, torch):
+    """Pre-marshalled C-ABI call per copy: the timed loop pays only the ctypes
+    call itself."""
+    L = fg.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    D = P(op["D"])
+    M, N, K, G = op["M"], op["N"], op["K"], op["G"]
+    calls = []
+    for c in copies:
+        if op["kind"] == "dense":
+            args = (P(c["A"]), P(c["sa"]), P(c["B"]), P(c["sb"]), D, M, N, K, stream)
+            calls.append((L.fg_gemm_fp8_nt, args))
+        elif op["kind"] == "contiguous":
+            args = (P(c["A"]), P(c["sa"]), P(c["B"]), P(c["sb"]), D, P(op["m_indices"]),
+                    M, N, K, G, stream)
+            calls.append((L.fg_grouped_contiguous, args))
+        else:
+            args = (P(c["A"]), P(c["sa"]), P(c["B"]), P(c["sb"]), D, P(op["masked_m"]),
+                    G, M, N, K, stream)
+            calls.append((L.fg_grouped_masked, args))
+
+    def step(i):
+        f, a = calls[i % len(calls)]
+        rc = f(*a)
+        if rc != 0:
+            raise RuntimeError(f"library call failed: {fg.strerror(rc)}")
+    return step
+
+
+def time_workload(name, steps, warmup, fg, torch):
+    op = gpu_operands(name, fg, torch)
+    copies = replicate(op, torch)
+    step = make_step(op, copies, fg, torch)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / steps
+    kern_ms = ev0.elapsed_time(ev1) / steps
+    layout = {"dense": 0, "contiguous": 1, "masked": 2}[op["kind"]]
+    bm, bn, grid = fg.select_config(layout, op["M"], op["N"], op["K"], op["G"])
+    res = dict(op=op, copies=len(copies), wall_ms=wall_ms, kern_ms=kern_ms,
+               tile=f"{bm}x{bn}", grid=grid, bytes=algorithmic_bytes(op))
+    del copies
+    return res
+
+
+def summarize(r):
+    op = r["op"]
+    tflops = op["flop"] / (r["wall_ms"] * 1e-3) / 1e12
+    kt = op["flop"] / (r["kern_ms"] * 1e-3) / 1e12
+    return dict(M=op["M"], N=op["N"], K=op["K"], G=op["G"], rows_out=op["rows_out"],
+                tile=r["tile"], grid=r["grid"], us_per_call=round(r["wall_ms"] * 1e3, 2),
+                kernel_us=round(r["kern_ms"] * 1e3, 2), tflops=round(tflops, 1),
+                pct_fp8_peak=round(100 * kt / PEAK_FP8_TFLOPS, 2),
+                hbm_gbps=round(r["bytes"] / (r["kern_ms"] * 1e-3) / 1e9, 1),
+                input_copies=r["copies"])
+
+
+# --------------------------------------------------------------- CPU baseline
+def cpu_baseline(name, target_s):
+    """The oracle as it stands (dequantise to fp64 + one fp64 GEMM per expert),
+    timed on this host for the headline workload. Inputs are quantised by the
+    oracle outside the timed region."""
+    import numpy as np
+    import oracle
+    import workloads
+
+    w = workloads.make(name)
+    if w["kind"] != "dense":
+        raise ValueError("CPU baseline is defined for the dense headline workload")
+    A, sa = oracle.quantize_act_1x128(w["a"])
+    B, sb = oracle.quantize_weight_128x128(w["b"])
+    flop = workloads.useful_flop(w)
+    reps, spent = 0, 0.0
+    while reps == 0 or (spent < target_s and reps < 50):
+        t0 = time.perf_counter()
+        oracle.ref_dense(A, sa, B, sb)
+        spent += time.perf_counter() - t0
+        reps += 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    return {"value": round(flop * reps / spent / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"full {name} problem ({A.shape[0]}x{B.shape[0]}x{A.shape[1]}), "
+                      f"{reps} repetition(s), {spent:.1f} s; dequantise + fp64 numpy GEMM; "
+                      f"host cpus {len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU path is not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_grouped_gemm_02_amd as fg
+
+    if not torch.cuda.is_available():
+        print("bench.py: no HIP device", file=sys.stderr)
+        sys.exit(1)
+    fg.lib()
+    head = time_workload(args.workload, args.steps, args.warmup, fg, torch)
+    hs = summarize(head)
+    op = head["op"]
+    value = op["flop"] / (head["wall_ms"] * 1e-3) / 1e12
+    kern_s = head["kern_ms"] * 1e-3
+    achieved_gbps = head["bytes"] / kern_s / 1e9
+    achieved_tflops = op["flop"] / kern_s / 1e12
+    # arithmetic intensity below the FP8 ridge point -> HBM is the roof
+    ridge = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    hbm_bound = op["flop"] / head["bytes"] < ridge
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved_tflops, 1), "peak": round(PEAK_FP8_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP8_TFLOPS, 4),
+                "traffic": None}
+    roof.update(kernel_us=hs["kernel_us"], algorithmic_bytes=head["bytes"],
+                flop=op["flop"], fp8_peak_frac=round(achieved_tflops / PEAK_FP8_TFLOPS, 4))
+    del head
+    torch.cuda.empty_cache()
+
+    per = {args.workload: hs}
+    if not args.headline_only:
+        for name in ORDER:
+            if name == args.workload:
+                continue
+            r = time_workload(name, max(5, args.steps // 2), max(2, args.warmup // 2), fg, torch)
+            per[name] = summarize(r)
+            del r
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+
+    line = {
+        "metric": "FP8 TFLOPS (dense + grouped MoE) and % of MI355X dense FP8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(hs["us_per_call"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "layout": op["kind"], "M": op["M"], "N": op["N"],
+                   "K": op["K"], "G": op["G"], "scales": "1x128 (A), 128x128 (B), fp32",
+                   "out": "bf16", "tile": hs["tile"], "input_copies": hs["input_copies"],
+                   "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_workload": per,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

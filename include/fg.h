@@ -120,6 +120,28 @@ int fg_select_config(int layout, int M, int N, int K, int G, int num_cus,
  * for tests and tile sweeps; process-wide, not thread-safe. */
 int fg_force_tile(int bm, int bn);
 
+/*
+ * fp32 -> E4M3 quantisation producing this library's operand layouts
+ * (2kiu.com DeepGEMM explainer, section 4.4: scales from the data's
+ * statistics, saturation of out-of-range values; zwzgs.cn DeepGEMM page,
+ * "Features > fine-grained scaling"). Per block: amax = max |x|;
+ * scale = amax / 448 (1 if amax == 0); code = nearest E4M3 of
+ * clamp(x / scale, -448, 448), ties to even, sign kept (so -tiny -> 0x80).
+ * Inputs must be finite. Asynchronous on `stream`; caller owns all buffers.
+ *
+ * Activations, 1x128 blocks: x [batch][M][K] fp32 (16-byte aligned),
+ *   q [batch][M][K] E4M3, sa [batch][K/128][M] fp32 (the GEMM's sa layout;
+ *   batch = 1 for dense/contiguous, G for masked). K % 128 == 0.
+ */
+int fg_quant_act_1x128(const float* x, void* q, float* sa, int batch, int M, int K,
+                       hipStream_t stream);
+
+/* Weights, 128x128 blocks: w [rows][K] fp32 with rows % 128 == 0 (a grouped
+ *   weight [G][N][K] is rows = G*N), q [rows][K] E4M3, sb [rows/128][K/128]
+ *   fp32 (= [G][N/128][K/128]). */
+int fg_quant_weight_128x128(const float* w, void* q, float* sb, int rows, int K,
+                            hipStream_t stream);
+
 /* Static, human-readable description of a return code. */
 const char* fg_strerror(int code);
 

@@ -46,10 +46,13 @@ def lib():
         L.fg_select_config.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
                                        ctypes.POINTER(i)]
         L.fg_force_tile.argtypes = [i, i]
+        L.fg_quant_act_1x128.argtypes = [vp, vp, vp, i, i, i, vp]
+        L.fg_quant_weight_128x128.argtypes = [vp, vp, vp, i, i, vp]
         L.fg_strerror.argtypes = [i]
         L.fg_strerror.restype = ctypes.c_char_p
         for name in ("fg_gemm_fp8_nt", "fg_grouped_contiguous", "fg_grouped_masked",
-                     "fg_select_config", "fg_force_tile"):
+                     "fg_select_config", "fg_force_tile", "fg_quant_act_1x128",
+                     "fg_quant_weight_128x128"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -164,3 +167,49 @@ def select_config(layout, M, N, K, G=1, num_cus=0):
 def force_tile(bm=0, bn=0):
     """Force a compiled tile shape for later calls; (0, 0) restores automatic choice."""
     _check(lib().fg_force_tile(bm, bn), "fg_force_tile")
+
+
+def quant_act_1x128(x, q=None, sa=None):
+    """fp32 activations [M, K] (or [batch, M, K]) -> (E4M3 codes, sa) with one scale per
+    1x128 block; sa comes out in the GEMM's layout [K/128, M] ([batch, K/128, M])."""
+    torch = _torch()
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be [M, K] or [batch, M, K]")
+    batch = x.shape[0] if x.dim() == 3 else 1
+    M, K = x.shape[-2], x.shape[-1]
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    _dev(x, "x", tuple(x.shape), torch.float32)
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    sa_shape = (batch, K // 128, M) if x.dim() == 3 else (K // 128, M)
+    if sa is None:
+        sa = torch.empty(sa_shape, dtype=torch.float32, device=x.device)
+    _fp8(q, "q", tuple(x.shape))
+    _dev(sa, "sa", sa_shape, torch.float32)
+    _check(lib().fg_quant_act_1x128(_ptr(x), _ptr(q), _ptr(sa), batch, M, K, _stream(x)),
+           "fg_quant_act_1x128")
+    return q, sa
+
+
+def quant_weight_128x128(w, q=None, sb=None):
+    """fp32 weights [N, K] (or [G, N, K]) -> (E4M3 codes, sb) with one scale per
+    128x128 block; sb is [N/128, K/128] ([G, N/128, K/128])."""
+    torch = _torch()
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [N, K] or [G, N, K]")
+    N, K = w.shape[-2], w.shape[-1]
+    if N % 128 or K % 128:
+        raise ValueError("N and K must be multiples of 128")
+    rows = w.numel() // K
+    _dev(w, "w", tuple(w.shape), torch.float32)
+    sb_shape = tuple(w.shape[:-2]) + (N // 128, K // 128)
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if sb is None:
+        sb = torch.empty(sb_shape, dtype=torch.float32, device=w.device)
+    _fp8(q, "q", tuple(w.shape))
+    _dev(sb, "sb", sb_shape, torch.float32)
+    _check(lib().fg_quant_weight_128x128(_ptr(w), _ptr(q), _ptr(sb), rows, K, _stream(w)),
+           "fg_quant_weight_128x128")
+    return q, sb

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfg.so")
-SOURCES = ["fg_host.hip"]
+SOURCES = ["fg_host.hip", "fg_quant.hip"]
 HEADERS = ["fg_kernel.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,153 @@
+// fg_quant.hip -- fp32 -> OCP E4M3 block quantisers producing the operands of
+// the block-scaled GEMM: one fp32 scale per 1x128 block of an activation and
+// per 128x128 block of a weight, scale = amax / 448, values divided by the
+// scale, clamped to [-448, 448] and rounded to nearest E4M3 with ties to even.
+//
+// Sources: the 2kiu.com DeepGEMM explainer, section 4.4 (scale factors derived
+// from the data's statistics; out-of-range values clipped/saturated) and the
+// zwzgs.cn DeepGEMM page, "Features > fine-grained scaling". The 1x128 and
+// 128x128 granularity, amax/448 and round-to-nearest-even are the readings
+// taken where the pages stop.
+//
+// Inputs must be finite. Both kernels are bandwidth-bound streaming passes:
+// each input byte is read once, each code byte written once.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fg.h"
+
+namespace {
+
+constexpr float kE4M3Max = 448.0f;
+
+// Nearest E4M3 code of y (|y| <= 448, finite), ties to the even code; the
+// sign bit is copied from y.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = __uint_as_float(bits & 0x7fffffffu);
+  uint32_t mag;
+  if (a < 0.015625f) {
+    // below the smallest normal 2^-6 the codes 0..8 are the multiples
+    // c * 2^-9; a * 512 is exact, rintf rounds half to even
+    mag = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    // keep 3 mantissa bits: round the fp32 significand at bit 20, half to even
+    uint32_t u = bits & 0x7fffffffu;
+    u += 0x7ffffu + ((u >> 20) & 1u);
+    const uint32_t e = (u >> 23) - 127u + 7u;  // E4M3 exponent field (1..15)
+    mag = (e << 3) | ((u >> 20) & 7u);
+  }
+  return sign | mag;
+}
+
+__device__ __forceinline__ float block_scale(float amax) {
+  return amax == 0.0f ? 1.0f : amax / kE4M3Max;   // IEEE division
+}
+
+__device__ __forceinline__ uint32_t encode4(float4 v, float s) {
+  const float lo = -kE4M3Max, hi = kE4M3Max;
+  const uint32_t c0 = e4m3_rne(fminf(fmaxf(v.x / s, lo), hi));
+  const uint32_t c1 = e4m3_rne(fminf(fmaxf(v.y / s, lo), hi));
+  const uint32_t c2 = e4m3_rne(fminf(fmaxf(v.z / s, lo), hi));
+  const uint32_t c3 = e4m3_rne(fminf(fmaxf(v.w / s, lo), hi));
+  return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+}
+
+__device__ __forceinline__ float amax4(float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// 1x128 blocks: 32 lanes per block (4 floats each), 8 blocks per 256-thread
+// workgroup. x [batch][M][K] -> q [batch][M][K], sa [batch][K/128][M].
+__global__ __launch_bounds__(256) void quant_act_1x128(const float* __restrict__ x,
+                                                       uint8_t* __restrict__ q,
+                                                       float* __restrict__ sa,
+                                                       int M, int K, long blocks) {
+  const long blk = (long)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (blk >= blocks) return;
+  const int l = threadIdx.x & 31;
+  const int KB = K / 128;
+  const long row = blk / KB;          // global row over batch*M
+  const int kb = (int)(blk - row * KB);
+  const long off = row * K + (long)kb * 128 + l * 4;
+  const float4 v = *(const float4*)(x + off);
+  float m = amax4(v);
+#pragma unroll
+  for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 32));
+  const float s = block_scale(m);
+  *(uint32_t*)(q + off) = encode4(v, s);
+  if (l == 0) {
+    const long b = row / M, r = row - b * M;
+    sa[(b * KB + kb) * (long)M + r] = s;
+  }
+}
+
+// 128x128 blocks: one 256-thread workgroup per block, 16 float4 per thread.
+// w [R][K] (R = G*N rows, a multiple of 128) -> q [R][K], sb [R/128][K/128].
+__global__ __launch_bounds__(256) void quant_weight_128x128(const float* __restrict__ w,
+                                                            uint8_t* __restrict__ q,
+                                                            float* __restrict__ sb, int K) {
+  __shared__ float red[8];
+  const int KB = K / 128;
+  const long br = blockIdx.x / KB;
+  const int kb = blockIdx.x - (int)(br * KB);
+  const int t = threadIdx.x;
+  const int col = (t & 31) * 4;       // 32 threads cover one 128-wide row
+  const int r0 = t >> 5;              // 8 rows per pass, 16 passes
+  float4 v[16];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const long row = br * 128 + r0 + i * 8;
+    v[i] = *(const float4*)(w + row * K + (long)kb * 128 + col);
+    m = fmaxf(m, amax4(v[i]));
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = block_scale(m);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const long row = br * 128 + r0 + i * 8;
+    *(uint32_t*)(q + row * K + (long)kb * 128 + col) = encode4(v[i], s);
+  }
+  if (t == 0) sb[br * KB + kb] = s;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+// Declared in fg.h.
+int fg_quant_act_1x128(const float* x, void* q, float* sa, int batch, int M, int K,
+                       hipStream_t stream) {
+  if (batch < 0 || M < 0 || K < 128 || K % 128) return FG_EINVAL;
+  if (batch == 0 || M == 0) return FG_OK;
+  if (!x || !q || !sa || !aligned(x, 16) || !aligned(q, 4) || !aligned(sa, 4)) return FG_EINVAL;
+  const long blocks = (long)batch * M * (K / 128);
+  const long grid = (blocks + 7) / 8;
+  if (grid > 0x7fffffffL) return FG_EINVAL;
+  hipLaunchKernelGGL(quant_act_1x128, dim3((unsigned)grid), dim3(256), 0, stream, x,
+                     static_cast<uint8_t*>(q), sa, M, K, blocks);
+  return hipGetLastError() == hipSuccess ? FG_OK : FG_ELAUNCH;
+}
+
+int fg_quant_weight_128x128(const float* w, void* q, float* sb, int rows, int K,
+                            hipStream_t stream) {
+  if (rows < 0 || rows % 128 || K < 128 || K % 128) return FG_EINVAL;
+  if (rows == 0) return FG_OK;
+  if (!w || !q || !sb || !aligned(w, 16) || !aligned(q, 4) || !aligned(sb, 4)) return FG_EINVAL;
+  const long grid = (long)(rows / 128) * (K / 128);
+  if (grid > 0x7fffffffL) return FG_EINVAL;
+  hipLaunchKernelGGL(quant_weight_128x128, dim3((unsigned)grid), dim3(256), 0, stream, w,
+                     static_cast<uint8_t*>(q), sb, K);
+  return hipGetLastError() == hipSuccess ? FG_OK : FG_ELAUNCH;
+}
+
+}  // extern "C"
