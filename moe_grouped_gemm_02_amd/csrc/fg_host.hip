@@ -41,9 +41,18 @@ int current_device(int* cus) {
 // ---------------------------------------------------------------- tiles
 struct Tile {
   int bm, bn;
+  double eff;   // relative MFMA efficiency of one tile (larger tiles reuse more)
 };
-// Compiled tile shapes (rows x cols of D per workgroup).
-constexpr Tile kTiles[] = {{128, 128}};
+// Compiled tile shapes (rows x cols of D per workgroup), in the order of the
+// launch switch below.
+using Cfg0 = fg::TileCfg<256, 256, 4, 2, 2, false>;   // large dense / grouped
+using Cfg1 = fg::TileCfg<256, 128, 4, 2, 3, false>;
+using Cfg2 = fg::TileCfg<128, 256, 2, 4, 3, false>;   // contiguous (BM | 128)
+using Cfg3 = fg::TileCfg<128, 128, 2, 2, 4, false>;
+using Cfg4 = fg::TileCfg<64, 112, 4, 1, 6, true>;     // skinny M, HBM-bound
+using Cfg5 = fg::TileCfg<256, 112, 4, 1, 3, true>;    // masked decode, HBM-bound
+constexpr Tile kTiles[] = {{256, 256, 1.00}, {256, 128, 0.95}, {128, 256, 0.95},
+                           {128, 128, 0.80}, {64, 112, 0.50},  {256, 112, 0.90}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kDefaultCUs = 256;
 
@@ -58,24 +67,26 @@ long count_tiles(int layout, int M, int N, int G, const Tile& t) {
   return (long)ceil_div(M, t.bm) * tn;
 }
 
-// Picks the tile index for a problem: among the compiled tiles, the one whose
-// tile count fills the CUs best (fraction of busy CU-slots over all waves),
-// preferring larger tiles on ties.
+// Picks the tile for a problem: the compiled shape with the smallest
+// estimated time, (waves of tiles over the CUs) x (tile area / tile
+// efficiency). The wave count carries the quantisation loss the zwzgs.cn
+// DeepGEMM page describes ("non-standard block sizes": a tile count just
+// above a multiple of the SM count leaves most of the last wave idle); the
+// area term carries the padding waste of partial tiles. Contiguous tiles must
+// not straddle an aligned 128-row expert block.
 int pick_tile(int layout, int M, int N, int G, int cus) {
   const int forced = g_forced_tile.load(std::memory_order_relaxed);
   if (forced >= 0) return forced;
-  int best = 0;
-  double best_eff = -1.0;
+  int best = -1;
+  double best_cost = 0.0;
   for (int i = 0; i < kNumTiles; ++i) {
     if (layout == FG_LAYOUT_CONTIGUOUS && 128 % kTiles[i].bm != 0) continue;
     const long tiles = count_tiles(layout, M, N, G, kTiles[i]);
     const long waves = (tiles + cus - 1) / cus;
-    const double eff = waves ? (double)tiles / (double)(waves * cus) : 0.0;
-    const double area = (double)kTiles[i].bm * kTiles[i].bn;
-    const double best_area = (double)kTiles[best].bm * kTiles[best].bn;
-    if (eff > best_eff + 1e-9 || (eff > best_eff - 1e-9 && area > best_area)) {
+    const double cost = (double)waves * kTiles[i].bm * kTiles[i].bn / kTiles[i].eff;
+    if (best < 0 || cost < best_cost * (1.0 - 1e-9)) {
       best = i;
-      best_eff = eff;
+      best_cost = cost;
     }
   }
   return best;
@@ -84,11 +95,13 @@ int pick_tile(int layout, int M, int N, int G, int cus) {
 template <int LAYOUT>
 hipError_t launch_layout(int tile, const Params& p, int grid, hipStream_t s) {
   switch (tile) {
-    case 0:
-      hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, 128, 128>), dim3(grid), dim3(fg::kThreads), 0, s, p);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 0: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg0>), dim3(grid), dim3(Cfg0::THREADS), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg1>), dim3(grid), dim3(Cfg1::THREADS), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg2>), dim3(grid), dim3(Cfg2::THREADS), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg3>), dim3(grid), dim3(Cfg3::THREADS), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg4>), dim3(grid), dim3(Cfg4::THREADS), 0, s, p); break;
+    case 5: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg5>), dim3(grid), dim3(Cfg5::THREADS), 0, s, p); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -108,6 +121,8 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
     return FG_EINVAL;
   if (m_indices && !aligned(m_indices, 4)) return FG_EINVAL;
   if (masked_m && !aligned(masked_m, 4)) return FG_EINVAL;
+  // the kernels address one expert's A or B with 32-bit byte offsets
+  if ((long long)M * K > 0x7fffffffLL || (long long)N * K > 0x7fffffffLL) return FG_EINVAL;
 
   int cus = 0;
   const int st = current_device(&cus);

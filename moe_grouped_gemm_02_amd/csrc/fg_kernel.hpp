@@ -9,7 +9,25 @@
 // Here every 128-wide K-block is one v_mfma_f32_16x16x128_f8f6f4 per 16x16
 // sub-tile with a zero C operand (a fresh FP32 partial covering exactly one
 // scale block), followed by one v_fma_f32 per output element that adds
-// partial * (sa * sb) into the master accumulator held in VGPRs.
+// partial * (sa * sb) into the master accumulator held in VGPRs. Each MFMA's
+// promotion is issued after the next MFMA, so the VALU work overlaps the
+// matrix core instead of waiting on it.
+//
+// Data movement (the pages' "data movement / compute / epilogue" overlap,
+// "Technical details > thread specialisation", done the gfx950 way): every
+// wave issues direct global->LDS loads (global_load_lds_dwordx4, no VGPR
+// staging) for its share of the next K-blocks into an S-stage ring of LDS
+// buffers, so there are no producer waves; one workgroup barrier per K-block
+// both publishes the next stage and frees the stage just consumed. The
+// barrier sits before the last column of MFMAs, so the next K-block's
+// fragments are read from LDS while those MFMAs run.
+//
+// LDS layout of a stage: A tile [BM rows][128 B], B tile [BN rows][128 B],
+// then BM activation scales (fp32). A 16-byte chunk c of tile row r is stored
+// at chunk position c ^ (r & 7) (XOR swizzle): the 16 rows a quarter-wave
+// reads for one chunk index hit distinct bank groups. The swizzle is applied
+// by choosing which global chunk each DMA lane fetches, since a DMA lane's LDS
+// destination is fixed (lane * 16 bytes after the wave's base).
 //
 // Operand roles. The MFMA's first operand is fed with rows of B (output
 // columns n), its second with rows of A (output rows m). The 16x16 result then
@@ -20,8 +38,7 @@
 // K order inside a fragment. The hardware sums a 128-long dot product; which
 // lane/byte holds which k does not change the sum as long as both operands use
 // the same placement. Lane l (row l % 16, quarter q = l / 16) holds bytes
-// [16q, 16q+16) and [64+16q, 64+16q+16) of its row's K-block, i.e. two 16-byte
-// LDS reads.
+// [16q, 16q+16) and [64+16q, 64+16q+16) of its row's K-block.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,11 +49,15 @@ namespace fg {
 typedef int   i32x4 __attribute__((ext_vector_type(4)));
 typedef int   i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(1))) const uint8_t gbl_u8;
+typedef __attribute__((address_space(3))) const float lds_f32;
 
 enum Layout { kDense = 0, kContiguous = 1, kMasked = 2 };
 
 constexpr int kKBlock = 128;   // scale block along K (elements == bytes)
-constexpr int kThreads = 256;  // 4 waves of 64
+constexpr int kXCDs = 8;       // MI355X: workgroups go round-robin to 8 XCDs
+constexpr int kGroupM = 4;     // m-blocks per rasterisation group
 
 struct Params {
   const uint8_t* A;       // E4M3 [rows][K] (masked: [G][M][K])
@@ -52,6 +73,38 @@ struct Params {
   int tiles_m, tiles_n;   // tile grid of one group
 };
 
+// Compile-time tile configuration.
+//   BM x BN   output tile per workgroup
+//   WGM x WGN waves per workgroup (each wave owns a (BM/WGM) x (BN/WGN) block)
+//   STAGES    depth of the LDS ring
+//   STRADDLE  a wave's columns may span two 128-wide scale blocks of B
+template <int BM_, int BN_, int WGM_, int WGN_, int STAGES_, bool STRADDLE_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, STAGES = STAGES_;
+  static constexpr bool STRADDLE = STRADDLE_;
+  static constexpr int W = WGM * WGN;
+  static constexpr int THREADS = 64 * W;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  // DMA instructions per wave per stage; padding slots load a clamped row.
+  static constexpr int A_INSTR = (BM * 8 + 64 * W - 1) / (64 * W);
+  static constexpr int B_INSTR = (BN * 8 + 64 * W - 1) / (64 * W);
+  static constexpr int SA_INSTR = (BM + 64 * W - 1) / (64 * W);
+  static constexpr int A_BYTES = A_INSTR * W * 1024;
+  static constexpr int B_BYTES = B_INSTR * W * 1024;
+  static constexpr int SA_BYTES = SA_INSTR * W * 256;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int DMA_PER_STAGE = A_INSTR + B_INSTR + SA_INSTR;
+  static_assert(WM % 16 == 0 && WN % 16 == 0 && TM >= 1 && TN >= 1, "wave tile must be 16-aligned");
+  static_assert(BM % WGM == 0 && BN % WGN == 0, "waves must split the tile evenly");
+  static_assert(STAGES >= 2, "need at least double buffering");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
+  static_assert((STAGES - 1) * DMA_PER_STAGE < 64, "vmcnt counter range");
+  static_assert(WN <= 128, "a wave's columns may touch at most two scale blocks");
+  static_assert(STRADDLE || 128 % WN == 0, "non-straddling waves must tile the 128-wide scale blocks");
+};
+
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   uint32_t u = __float_as_uint(f);
@@ -60,41 +113,101 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return u >> 16;
 }
 
-// 16-byte chunk c (0..7) of tile row r lives at chunk c ^ (r & 7): the eight
-// rows a quarter-wave reads for one chunk index land in eight different
-// 16-byte bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kKBlock + ((chunk ^ (row & 7)) << 4);
 }
 
-template <int LAYOUT, int BM, int BN>
-__global__ __launch_bounds__(kThreads) void fp8_bs_gemm(Params p) {
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "tile must split into 2x2 waves of 16-row sub-tiles");
-  constexpr int WM = BM / 2, WN = BN / 2;   // wave tile
-  constexpr int TM = WM / 16, TN = WN / 16; // 16x16 sub-tiles per wave
-  constexpr int LA = BM * 8 / kThreads;     // 16-byte A chunks per thread per K-block
-  constexpr int LB = BN * 8 / kThreads;
-  static_assert(LA >= 1 && LB >= 1, "tile too small for the loader");
+// Wait until at most N of this wave's vector-memory operations are in flight
+// (the LDS-DMA loads complete in issue order), then stop the compiler from
+// moving LDS accesses across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * kKBlock];
+// Target builtins live in __device__ helpers: the lambdas below are
+// host+device, and a gfx950 builtin inside one would make the host-side
+// instantiation of the kernel (its launch stub) silently fail.
+__device__ __forceinline__ void dma16(const uint8_t* src, lds_u8* dst) {
+  __builtin_amdgcn_global_load_lds((gbl_u8*)src, dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const uint8_t* src, lds_u8* dst) {
+  __builtin_amdgcn_global_load_lds((gbl_u8*)src, dst, 4, 0, 0);
+}
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// Keep one pipeline step's order -- the MFMA first, then its LDS reads, then
+// the VALU promotion of the previous partial -- and let nothing cross steps.
+__device__ __forceinline__ void step_fence() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ i32x8 frag_read(const lds_u8* tile, int row, int lq) {
+  const i32x4 lo = *(const __attribute__((address_space(3))) i32x4*)(tile + swz(row, lq));
+  const i32x4 hi = *(const __attribute__((address_space(3))) i32x4*)(tile + swz(row, lq + 4));
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ f32x4 mfma_e4m3(const i32x8& b_rows, const i32x8& a_rows) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // cbsz = blgp = 0 selects E4M3 for both operands; C = 0 starts a fresh partial
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b_rows, a_rows, zero, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void promote(f32x4& acc, const f32x4& part, float s) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(part[r], s, acc[r]);
+}
+
+template <int LAYOUT, class T>
+__global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
+  constexpr int BM = T::BM, BN = T::BN, W = T::W, WM = T::WM, WN = T::WN;
+  constexpr int TM = T::TM, TN = T::TN, S = T::STAGES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
   __shared__ int s_group;
+  lds_u8* const lds = (lds_u8*)smem;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = uniform(t >> 6);
+  const int wm = wave / T::WGN, wn = wave % T::WGN;
   const int lr = lane & 15, lq = lane >> 4;
 
-  // ---- tile -> (group, m-block, n-block)
-  int tile = blockIdx.x;
+  // ---- workgroup -> tile. Consecutive tile ids are placed on the same XCD
+  // (workgroups are dealt round-robin to the XCDs), then tiles are walked in
+  // groups of kGroupM m-blocks so the tiles resident on one XCD share A rows
+  // and B columns in its L2.
+  int tile;
+  {
+    const int b = blockIdx.x, nwg = gridDim.x;
+    const int x = b % kXCDs, l = b / kXCDs;
+    const int per = nwg / kXCDs, rem = nwg % kXCDs;
+    tile = x * per + (x < rem ? x : rem) + l;
+  }
   int g = 0;
   if (LAYOUT == kMasked) {
     const int per = p.tiles_m * p.tiles_n;
     g = tile / per;
     tile -= g * per;
   }
-  const int mb = tile / p.tiles_n;
-  const int nbk = tile - mb * p.tiles_n;
+  int mb, nbk;
+  {
+    const int span = kGroupM * p.tiles_n;
+    const int grp = tile / span;
+    const int first = grp * kGroupM;
+    const int gsz = min(kGroupM, p.tiles_m - first);
+    const int in = tile - grp * span;
+    mb = first + in % gsz;
+    nbk = in / gsz;
+  }
   const int m0 = mb * BM, n0 = nbk * BN;
 
   int rows_valid = p.M;  // rows of this slab that have an output
@@ -115,61 +228,63 @@ __global__ __launch_bounds__(kThreads) void fp8_bs_gemm(Params p) {
     g = s_group;
     if (g < 0) return;  // all-padding block
   }
+  g = uniform(g);
 
-  const size_t K = (size_t)p.K;
-  const int KB = p.KB;
-  const uint8_t* Ag = p.A + (LAYOUT == kMasked ? (size_t)g * p.M * K : 0);
-  const float* sag = p.sa + (LAYOUT == kMasked ? (size_t)g * KB * p.M : 0);
+  const int K = p.K, KB = p.KB, M = p.M;
+  const uint8_t* Ag = p.A + (LAYOUT == kMasked ? (size_t)g * M * K : 0);
+  const float* sag = p.sa + (LAYOUT == kMasked ? (size_t)g * KB * M : 0);
   const uint8_t* Bg = p.B + (LAYOUT != kDense ? (size_t)g * p.N * K : 0);
   const float* sbg = p.sb + (LAYOUT != kDense ? (size_t)g * (p.N / 128) * KB : 0);
-  uint16_t* Dg = p.D + (LAYOUT == kMasked ? (size_t)g * p.M * p.N : 0);
+  uint16_t* Dg = p.D + (LAYOUT == kMasked ? (size_t)g * M * p.N : 0);
 
-  // ---- global -> register staging of one K-block (rows clamped into range;
-  // clamped rows are computed but never stored)
-  i32x4 ra[LA], rb[LB];
-  const uint8_t* a_src[LA];
-  const uint8_t* b_src[LB];
-  int a_dst[LA], b_dst[LB];
+  // ---- per-lane DMA sources (byte offsets within one K-block column).
+  // Slot s of a region is the 16-byte LDS chunk s; it holds row s/8, chunk
+  // position s%8, i.e. global chunk (s%8) ^ (row%8). Rows past the tile
+  // (padding slots) and past the matrix are clamped to a valid row.
+  uint32_t a_off[T::A_INSTR], b_off[T::B_INSTR], sa_off[T::SA_INSTR];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int c = t + kThreads * i, row = c >> 3, col = c & 7;
-    const int m = min(m0 + row, p.M - 1);
-    a_src[i] = Ag + (size_t)m * K + col * 16;
-    a_dst[i] = swz(row, col);
+  for (int q = 0; q < T::A_INSTR; ++q) {
+    const int slot = (q * W + wave) * 64 + lane;
+    const int row = slot >> 3, chunk = (slot & 7) ^ (row & 7);
+    const int m = min(m0 + min(row, BM - 1), M - 1);
+    a_off[q] = (uint32_t)m * (uint32_t)K + chunk * 16;
   }
 #pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int c = t + kThreads * i, row = c >> 3, col = c & 7;
-    const int n = min(n0 + row, p.N - 1);
-    b_src[i] = Bg + (size_t)n * K + col * 16;
-    b_dst[i] = BM * kKBlock + swz(row, col);
+  for (int q = 0; q < T::B_INSTR; ++q) {
+    const int slot = (q * W + wave) * 64 + lane;
+    const int row = slot >> 3, chunk = (slot & 7) ^ (row & 7);
+    const int n = min(n0 + min(row, BN - 1), p.N - 1);
+    b_off[q] = (uint32_t)n * (uint32_t)K + chunk * 16;
+  }
+#pragma unroll
+  for (int q = 0; q < T::SA_INSTR; ++q) {
+    const int idx = (q * W + wave) * 64 + lane;
+    sa_off[q] = (uint32_t)min(m0 + min(idx, BM - 1), M - 1) * 4u;
   }
 
-  // scales this lane needs: one sa per sub-tile row, one sb per sub-tile column
-  int sa_row[TM];
+  auto issue = [&](int kb, int stage) {
+    lds_u8* const base = lds + stage * T::STAGE_BYTES;
+    const uint8_t* const ak = Ag + (size_t)kb * kKBlock;
+    const uint8_t* const bk = Bg + (size_t)kb * kKBlock;
+    const uint8_t* const sk = (const uint8_t*)(sag + (size_t)kb * M);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) sa_row[i] = min(m0 + wm * WM + i * 16 + lr, p.M - 1);
-  int sb_blk[TN];
+    for (int q = 0; q < T::A_INSTR; ++q) dma16(ak + a_off[q], base + (q * W + wave) * 1024);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) sb_blk[j] = min((n0 + wn * WN + j * 16) >> 7, p.N / 128 - 1) * KB;
+    for (int q = 0; q < T::B_INSTR; ++q) dma16(bk + b_off[q], base + T::A_BYTES + (q * W + wave) * 1024);
+#pragma unroll
+    for (int q = 0; q < T::SA_INSTR; ++q) dma4(sk + sa_off[q], base + T::A_BYTES + T::B_BYTES + (q * W + wave) * 256);
+  };
 
-  float sa_nx[TM], sb_nx[TN];
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i) ra[i] = *(const i32x4*)(a_src[i] + (size_t)kb * kKBlock);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) rb[i] = *(const i32x4*)(b_src[i] + (size_t)kb * kKBlock);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) sa_nx[i] = sag[(size_t)kb * p.M + sa_row[i]];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) sb_nx[j] = sbg[sb_blk[j] + kb];
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i) *(i32x4*)(&lds[buf][a_dst[i]]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < LB; ++i) *(i32x4*)(&lds[buf][b_dst[i]]) = rb[i];
-  };
+  // ---- scale blocks of B covered by this wave's columns (at most two)
+  const int wn0 = n0 + wn * WN;
+  const int nb_lo = uniform(min(wn0 >> 7, p.N / 128 - 1));
+  const int nb_hi = uniform(min(nb_lo + 1, p.N / 128 - 1));
+  // first sub-tile column whose scale block is nb_hi
+  const int j_switch = T::STRADDLE ? uniform(((nb_lo + 1) * 128 - wn0) >> 4) : TN;
+
+  // rows this wave owns that have an output (a wave with none still computes
+  // on clamped rows to keep the schedule branch-free, but stores nothing)
+  const bool wave_active = m0 + wm * WM < rows_valid;
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -177,61 +292,83 @@ __global__ __launch_bounds__(kThreads) void fp8_bs_gemm(Params p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  float sa_cur[TM], sb_cur[TN];
+  // ---- prologue: fill the ring (K-blocks past the end are clamped loads that
+  // keep every wave's DMA count uniform), wait for stage 0
 #pragma unroll
-  for (int i = 0; i < TM; ++i) sa_cur[i] = sa_nx[i];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) sb_cur[j] = sb_nx[j];
-  lstore(0);
-  __syncthreads();
+  for (int s = 0; s < S; ++s) issue(min(s, KB - 1), s);
+  wait_vm<(S - 1) * T::DMA_PER_STAGE>();
+  block_barrier();
 
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < KB; ++kb) {
-    const int cur = kb & 1;
-    const bool more = kb + 1 < KB;
-    if (more) gload(kb + 1);
-
-    i32x8 fa[TM], fb[TN];
+  i32x8 fa[TM], fb;
+  float s_lo[TM], s_hi[TM];
+  auto load_scales = [&](const lds_u8* st, int kb) {
+    lds_f32* sas = (lds_f32*)(st + T::A_BYTES + T::B_BYTES);
+    const float b0 = sbg[uniform(nb_lo * KB + kb)];
+    const float b1 = sbg[uniform(nb_hi * KB + kb)];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int row = wm * WM + i * 16 + lr;
-      const i32x4 lo = *(const i32x4*)(&lds[cur][swz(row, lq)]);
-      const i32x4 hi = *(const i32x4*)(&lds[cur][swz(row, lq + 4)]);
-      fa[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const float a = sas[wm * WM + i * 16 + lr];
+      s_lo[i] = a * b0;
+      s_hi[i] = T::STRADDLE ? a * b1 : 0.f;
     }
+  };
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row = wn * WN + j * 16 + lr;
-      const i32x4 lo = *(const i32x4*)(&lds[cur][BM * kKBlock + swz(row, lq)]);
-      const i32x4 hi = *(const i32x4*)(&lds[cur][BM * kKBlock + swz(row, lq + 4)]);
-      fb[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
+  for (int i = 0; i < TM; ++i) fa[i] = frag_read(lds, wm * WM + i * 16 + lr, lq);
+  fb = frag_read(lds + T::A_BYTES, wn * WN + lr, lq);
+  load_scales(lds, 0);
 
+  // One K-block: TM x TN MFMAs in column order. Step u issues MFMA u and then
+  // promotes MFMA u-1 (already complete by then), so the FMAs run under the
+  // next MFMA. Column j+1's B fragment is read at the start of column j. The
+  // barrier precedes the last column; after it the next stage's A fragments
+  // replace each fa[i] as soon as its last MFMA has been issued. ISSUE = false is
+  // the tail (no DMA left to issue; wait for everything outstanding).
+  int stage = 0;
+  auto kblock = [&](int kb, bool ISSUE) {
+    const int nstage = stage + 1 == S ? 0 : stage + 1;
+    const lds_u8* cur = lds + stage * T::STAGE_BYTES;
+    const lds_u8* nxt = lds + nstage * T::STAGE_BYTES;
+    f32x4 part[2];
+    i32x8 fb_next;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        // fresh FP32 partial of this K-block (C = 0), format 0 = E4M3 for both
-        const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            fb[j], fa[i], zero, 0, 0, 0, 0, 0, 0);
-        const float s = sa_cur[i] * sb_cur[j];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], s, acc[i][j][r]);
+    for (int u = 0; u < TM * TN; ++u) {
+      const int j = u / TM, i = u % TM;
+      if (j == TN - 1 && i == 0) {
+        // every read of the current stage has been issued: publish the next
+        // stage and recycle this one
+        wait_lgkm0();
+        if (ISSUE) wait_vm<(S - 2) * T::DMA_PER_STAGE>();
+        else wait_vm<0>();
+        block_barrier();
+        if (ISSUE) issue(kb + S, stage);
+        fb_next = frag_read(nxt + T::A_BYTES, wn * WN + lr, lq);
       }
+      part[u & 1] = mfma_e4m3(fb, fa[i]);
+      if (i == 0 && j + 1 < TN) fb_next = frag_read(cur + T::A_BYTES, wn * WN + (j + 1) * 16 + lr, lq);
+      if (j == TN - 1) fa[i] = frag_read(nxt, wm * WM + i * 16 + lr, lq);
+      if (u > 0) {
+        const int pj = (u - 1) / TM, pi = (u - 1) % TM;
+        const float s = (!T::STRADDLE || pj < j_switch) ? s_lo[pi] : s_hi[pi];
+        promote(acc[pi][pj], part[(u - 1) & 1], s);
+      }
+      if (i == TM - 1) fb = fb_next;
+      step_fence();
     }
+    {
+      constexpr int u = TM * TN - 1;
+      const float s = (!T::STRADDLE || TN - 1 < j_switch) ? s_lo[TM - 1] : s_hi[TM - 1];
+      promote(acc[TM - 1][TN - 1], part[u & 1], s);
+    }
+    load_scales(nxt, min(kb + 1, KB - 1));
+    stage = nstage;
+  };
 
-    if (more) {
-      lstore(cur ^ 1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) sa_cur[i] = sa_nx[i];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) sb_cur[j] = sb_nx[j];
-    }
-    __syncthreads();
-  }
+  int kb = 0;
+  for (; kb + S < KB; ++kb) kblock(kb, true);
+  for (; kb < KB; ++kb) kblock(kb, false);
 
   // ---- epilogue: bf16 RNE, one 8-byte store per lane per sub-tile
+  if (!wave_active) return;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m = m0 + wm * WM + i * 16 + lr;

@@ -1,0 +1,111 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fg.h declares, rejects invalid arguments before touching the device,
+and the host-side tile selection is sane."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_grouped_gemm_02_amd as fg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fg.h")
+EINVAL, OK = -1, 0
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fg_gemm_fp8_nt", "fg_grouped_contiguous", "fg_grouped_masked",
+              "fg_select_config", "fg_strerror", "fg_quant_act_1x128", "fg_quant_weight_128x128"):
+        assert n in names
+
+
+def test_library_loads_and_exports_everything_declared():
+    L = ctypes.CDLL(fg.LIB_PATH, mode=os.RTLD_NOW)   # unresolved symbols fail here
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_strerror_codes():
+    for c in (0, -1, -2, -3, -4, 17):
+        assert isinstance(fg.strerror(c), str) and fg.strerror(c)
+    assert "invalid" in fg.strerror(-1)
+
+
+BAD = ctypes.c_void_p(0x1001)      # misaligned, never dereferenced
+GOOD = ctypes.c_void_p(0x100000)   # aligned, never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("args", [
+    (GOOD, GOOD, GOOD, GOOD, GOOD, 64, 256, 100, None),       # K not a multiple of 128
+    (GOOD, GOOD, GOOD, GOOD, GOOD, 64, 200, 256, None),       # N not a multiple of 128
+    (GOOD, GOOD, GOOD, GOOD, GOOD, -1, 256, 256, None),       # negative M
+    (GOOD, GOOD, GOOD, GOOD, GOOD, 64, 256, 0, None),         # K < 128
+    (None, GOOD, GOOD, GOOD, GOOD, 64, 256, 256, None),       # null A
+    (GOOD, GOOD, GOOD, GOOD, None, 64, 256, 256, None),       # null D
+    (BAD, GOOD, GOOD, GOOD, GOOD, 64, 256, 256, None),        # misaligned A
+    (GOOD, GOOD, GOOD, GOOD, BAD, 64, 256, 256, None),        # misaligned D
+    (GOOD, GOOD, GOOD, GOOD, GOOD, 1 << 20, 256, 4096, None),  # M*K beyond 2^31
+])
+def test_dense_validation(args):
+    assert fg.lib().fg_gemm_fp8_nt(*args) == EINVAL
+
+
+def test_empty_problems_are_no_ops():
+    L = fg.lib()
+    assert L.fg_gemm_fp8_nt(None, None, None, None, None, 0, 256, 256, None) == OK
+    assert L.fg_gemm_fp8_nt(None, None, None, None, None, 64, 0, 256, None) == OK
+    assert L.fg_grouped_contiguous(None, None, None, None, None, None, 0, 256, 256, 4, None) == OK
+
+
+def test_grouped_validation():
+    L = fg.lib()
+    # G < 1
+    assert L.fg_grouped_contiguous(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 256, 256, 0, None) == EINVAL
+    assert L.fg_grouped_masked(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 0, 64, 256, 256, None) == EINVAL
+    # missing index arrays
+    assert L.fg_grouped_contiguous(GOOD, GOOD, GOOD, GOOD, GOOD, None, 64, 256, 256, 2, None) == EINVAL
+    assert L.fg_grouped_masked(GOOD, GOOD, GOOD, GOOD, GOOD, None, 2, 64, 256, 256, None) == EINVAL
+    # misaligned masked_m
+    assert L.fg_grouped_masked(GOOD, GOOD, GOOD, GOOD, GOOD, ctypes.c_void_p(0x100002), 2, 64, 256, 256,
+                               None) == EINVAL
+
+
+def test_quant_validation():
+    L = fg.lib()
+    assert L.fg_quant_act_1x128(GOOD, GOOD, GOOD, 1, 64, 100, None) == EINVAL
+    assert L.fg_quant_act_1x128(BAD, GOOD, GOOD, 1, 64, 128, None) == EINVAL
+    assert L.fg_quant_weight_128x128(GOOD, GOOD, GOOD, 100, 128, None) == EINVAL
+    assert L.fg_quant_act_1x128(None, None, None, 1, 0, 128, None) == OK
+
+
+def test_select_config_fills_the_machine():
+    # every choice must be a compiled tile and give a sane grid
+    for layout, M, N, K, G in [(0, 256, 7168, 7168, 1), (0, 8192, 7168, 18432, 1), (0, 128, 256, 512, 1),
+                               (1, 9472, 4096, 7168, 8), (2, 256, 7168, 2048, 16)]:
+        bm, bn, grid = fg.select_config(layout, M, N, K, G)
+        assert bm > 0 and bn > 0 and N % 16 == 0
+        tiles = -(-M // bm) * -(-N // bn) * (G if layout == 2 else 1)
+        assert grid == tiles
+        if layout == 1:
+            assert 128 % bm == 0         # contiguous tiles never straddle an expert block
+
+
+def test_select_config_rejects_bad_layout():
+    with pytest.raises(fg.FGError):
+        fg.select_config(7, 128, 128, 128)
+
+
+def test_force_tile_roundtrip():
+    fg.force_tile(128, 128)
+    assert fg.select_config(0, 8192, 7168, 18432)[:2] == (128, 128)
+    fg.force_tile(0, 0)
+    with pytest.raises(fg.FGError):
+        fg.force_tile(96, 96)

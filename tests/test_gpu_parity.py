@@ -140,3 +140,55 @@ def test_masked_nan_rows_beyond_count_do_not_leak():
     ref, valid = oracle.ref_masked(A, sa, B, sb, mm)
     r = oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
     assert r["ok"], r
+
+
+TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (64, 112), (256, 112)]
+
+
+@pytest.fixture
+def forced_tile(request):
+    bm, bn = request.param
+    fg.force_tile(bm, bn)
+    yield bm, bn
+    fg.force_tile(0, 0)
+
+
+@pytest.mark.parametrize("forced_tile", TILES, indirect=True, ids=lambda t: f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("K", [640, 1152])
+def test_every_tile_dense(forced_tile, K):
+    """Ragged M and N (N=512 is not a multiple of 112 or 256), K shorter and
+    longer than the deepest LDS ring."""
+    print(f"tile {forced_tile} dense K={K}", flush=True)
+    A, sa, B, sb = make_dense(300, 512, K, 60 + K)
+    out = run_dense(A, sa, B, sb)
+    r = oracle.check(out, oracle.ref_dense(A, sa, B, sb))
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("forced_tile", TILES, indirect=True, ids=lambda t: f"{t[0]}x{t[1]}")
+def test_every_tile_masked(forced_tile):
+    print(f"tile {forced_tile} masked", flush=True)
+    G, M_max, N, K = 3, 200, 384, 768
+    A, sa, B, sb, _ = make_masked(G, M_max, N, K, 61)
+    mm = np.array([77, 0, 200], np.int32)
+    Ad, sad, Bd, sbd = masked_inputs(A, sa, B, sb)
+    D = new_out((G, M_max, N))
+    fg.grouped_masked(Ad, sad, Bd, sbd, D, to_dev(mm))
+    torch.cuda.synchronize()
+    ref, valid = oracle.ref_masked(A, sa, B, sb, mm)
+    r = oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("forced_tile", [t for t in TILES if 128 % t[0] == 0], indirect=True,
+                         ids=lambda t: f"{t[0]}x{t[1]}")
+def test_every_tile_contiguous(forced_tile):
+    print(f"tile {forced_tile} contiguous", flush=True)
+    A, sa, B, sb, mi = make_contiguous(3, 384, 640, 62, m_lo=1, m_hi=300)
+    Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
+    D = new_out((A.shape[0], 384))
+    fg.grouped_contiguous(Ad, sad, Bd, sbd, D, to_dev(mi))
+    torch.cuda.synchronize()
+    ref, valid = oracle.ref_contiguous(A, sa, B, sb, mi)
+    r = oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
+    assert r["ok"], r
