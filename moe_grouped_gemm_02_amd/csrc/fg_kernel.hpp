@@ -23,7 +23,9 @@
 // fragments are read from LDS while those MFMAs run.
 //
 // LDS layout of a stage: A tile [BM rows][128 B], B tile [BN rows][128 B],
-// then BM activation scales (fp32). A 16-byte chunk c of tile row r is stored
+// then BM activation scales and the weight scales of the tile's 128-column
+// blocks (fp32), so every operand of a K-block arrives through the same
+// counted DMA stream. A 16-byte chunk c of tile row r is stored
 // at chunk position c ^ (r & 7) (XOR swizzle): the 16 rows a quarter-wave
 // reads for one chunk index hit distinct bank groups. The swizzle is applied
 // by choosing which global chunk each DMA lane fetches, since a DMA lane's LDS
@@ -49,6 +51,7 @@ namespace fg {
 typedef int   i32x4 __attribute__((ext_vector_type(4)));
 typedef int   i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(1))) const uint8_t gbl_u8;
 typedef __attribute__((address_space(3))) const float lds_f32;
@@ -89,19 +92,22 @@ struct TileCfg {
   // DMA instructions per wave per stage; padding slots load a clamped row.
   static constexpr int A_INSTR = (BM * 8 + 64 * W - 1) / (64 * W);
   static constexpr int B_INSTR = (BN * 8 + 64 * W - 1) / (64 * W);
-  static constexpr int SA_INSTR = (BM + 64 * W - 1) / (64 * W);
+  static constexpr int SB_SLOTS = 4;   // weight scales of the tile's (up to 3) 128-column blocks
+  static constexpr int SA_INSTR = (BM + SB_SLOTS + 64 * W - 1) / (64 * W);
   static constexpr int A_BYTES = A_INSTR * W * 1024;
   static constexpr int B_BYTES = B_INSTR * W * 1024;
   static constexpr int SA_BYTES = SA_INSTR * W * 256;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES;
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int ROWB = BN * 2 + 16;   // staged bf16 output row (+16 B against bank conflicts)
+  static constexpr int LDS_BYTES = RING_BYTES > BM * ROWB ? RING_BYTES : BM * ROWB;
   static constexpr int DMA_PER_STAGE = A_INSTR + B_INSTR + SA_INSTR;
   static_assert(WM % 16 == 0 && WN % 16 == 0 && TM >= 1 && TN >= 1, "wave tile must be 16-aligned");
   static_assert(BM % WGM == 0 && BN % WGN == 0, "waves must split the tile evenly");
   static_assert(STAGES >= 2, "need at least double buffering");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
-  static_assert((STAGES - 1) * DMA_PER_STAGE < 64, "vmcnt counter range");
   static_assert(WN <= 128, "a wave's columns may touch at most two scale blocks");
+  static_assert(TN >= 2, "the B-fragment ring needs at least two sub-tile columns per wave");
   static_assert(STRADDLE || 128 % WN == 0, "non-straddling waves must tile the 128-wide scale blocks");
 };
 
@@ -134,11 +140,20 @@ __device__ __forceinline__ void block_barrier() {
 // Target builtins live in __device__ helpers: the lambdas below are
 // host+device, and a gfx950 builtin inside one would make the host-side
 // instantiation of the kernel (its launch stub) silently fail.
-__device__ __forceinline__ void dma16(const uint8_t* src, lds_u8* dst) {
-  __builtin_amdgcn_global_load_lds((gbl_u8*)src, dst, 16, 0, 0);
+//
+// The LDS-DMA loads are issued through inline asm. When the compiler sees an
+// LDS-DMA in flight it can no longer count LDS reads precisely and waits for
+// all of them (lgkmcnt(0)) before every fragment use; hidden from it, the DMA
+// is tracked only by this kernel's explicit vmcnt waits, and the compiler's
+// lgkmcnt waits cover exactly the fragment reads. M0 holds the wave-uniform
+// LDS destination; one wait state separates its write from the DMA.
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, lds_u8* dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"((uint32_t)(uintptr_t)dst) : "memory");
 }
-__device__ __forceinline__ void dma4(const uint8_t* src, lds_u8* dst) {
-  __builtin_amdgcn_global_load_lds((gbl_u8*)src, dst, 4, 0, 0);
+__device__ __forceinline__ void dma4(const uint8_t* addr, lds_u8* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(addr), "s"((uint32_t)(uintptr_t)dst) : "memory");
 }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 // Keep one pipeline step's order -- the MFMA first, then its LDS reads, then
@@ -256,23 +271,32 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
     const int n = min(n0 + min(row, BN - 1), p.N - 1);
     b_off[q] = (uint32_t)n * (uint32_t)K + chunk * 16;
   }
+  // scale slots: [0, BM) activation rows, [BM, BM+4) weight blocks from the
+  // tile's first 128-column block on (clamped), the rest duplicate a row
+  const int nb_tile = n0 >> 7;
+  bool sa_is_sb[T::SA_INSTR];
 #pragma unroll
   for (int q = 0; q < T::SA_INSTR; ++q) {
     const int idx = (q * W + wave) * 64 + lane;
-    sa_off[q] = (uint32_t)min(m0 + min(idx, BM - 1), M - 1) * 4u;
+    sa_is_sb[q] = idx >= BM && idx < BM + T::SB_SLOTS;
+    sa_off[q] = sa_is_sb[q] ? (uint32_t)min(nb_tile + idx - BM, p.N / 128 - 1) * (uint32_t)KB * 4u
+                            : (uint32_t)min(m0 + min(idx, BM - 1), M - 1) * 4u;
   }
 
-  auto issue = [&](int kb, int stage) {
+  // One DMA instruction d (0 .. DMA_PER_STAGE-1) of K-block kb into a stage:
+  // A chunks first, then B chunks, then the scale slots.
+  auto issue_one = [&](int kb, int stage, int d) {
     lds_u8* const base = lds + stage * T::STAGE_BYTES;
-    const uint8_t* const ak = Ag + (size_t)kb * kKBlock;
-    const uint8_t* const bk = Bg + (size_t)kb * kKBlock;
-    const uint8_t* const sk = (const uint8_t*)(sag + (size_t)kb * M);
-#pragma unroll
-    for (int q = 0; q < T::A_INSTR; ++q) dma16(ak + a_off[q], base + (q * W + wave) * 1024);
-#pragma unroll
-    for (int q = 0; q < T::B_INSTR; ++q) dma16(bk + b_off[q], base + T::A_BYTES + (q * W + wave) * 1024);
-#pragma unroll
-    for (int q = 0; q < T::SA_INSTR; ++q) dma4(sk + sa_off[q], base + T::A_BYTES + T::B_BYTES + (q * W + wave) * 256);
+    if (d < T::A_INSTR) {
+      dma16(Ag + (size_t)kb * kKBlock, a_off[d], base + (d * W + wave) * 1024);
+    } else if (d < T::A_INSTR + T::B_INSTR) {
+      const int q = d - T::A_INSTR;
+      dma16(Bg + (size_t)kb * kKBlock, b_off[q], base + T::A_BYTES + (q * W + wave) * 1024);
+    } else {
+      const int q = d - T::A_INSTR - T::B_INSTR;
+      const uint8_t* const src = sa_is_sb[q] ? (const uint8_t*)(sbg + kb) : (const uint8_t*)(sag + (size_t)kb * M);
+      dma4(src + sa_off[q], base + T::A_BYTES + T::B_BYTES + (q * W + wave) * 256);
+    }
   };
 
   // ---- scale blocks of B covered by this wave's columns (at most two)
@@ -282,106 +306,165 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   // first sub-tile column whose scale block is nb_hi
   const int j_switch = T::STRADDLE ? uniform(((nb_lo + 1) * 128 - wn0) >> 4) : TN;
 
-  // rows this wave owns that have an output (a wave with none still computes
-  // on clamped rows to keep the schedule branch-free, but stores nothing)
-  const bool wave_active = m0 + wm * WM < rows_valid;
-
   f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: fill the ring (K-blocks past the end are clamped loads that
-  // keep every wave's DMA count uniform), wait for stage 0
+  // ---- DMA schedule. K-block x lands in stage x % S. Its stage is freed at
+  // the barrier of K-block x-S and must be complete at the barrier of K-block
+  // x-1. With S >= 3 its instructions are spread one per pipeline step over
+  // the K-block after the freeing barrier ("head" after that barrier, "tail"
+  // before the next one), leaving a further full K-block for the loads to
+  // land; with S = 2 they are spread over the steps right after the freeing
+  // barrier. Spreading keeps the MFMA pipe fed instead of stalling every wave
+  // on a burst of DMA issue. K-block indices past the end are clamped (those
+  // repeat loads hit L2), which keeps every wave's DMA count a compile-time
+  // constant for the vmcnt waits.
+  constexpr int STEPS = TM * TN;
+  constexpr int JB = TN - 2;          // the barrier precedes sub-tile column JB
+  constexpr int PRE = JB * TM;        // pipeline steps before the barrier
+  constexpr int POST = STEPS - PRE;   // pipeline steps after it
+  constexpr int D = T::DMA_PER_STAGE;
+  auto dma_slot = [](int d) constexpr { return S >= 3 ? d * STEPS / D : d * POST / D; };
+  constexpr int N_HEAD = [] {
+    int n = 0;
+    for (int d = 0; d < D; ++d) n += (S >= 3 ? d * STEPS / D : d * POST / D) < POST;
+    return n;
+  }();
+  static_assert((S - 2) * D + N_HEAD < 64, "vmcnt counter range");
+
+  // ---- prologue: K-blocks 0 .. S-2 and the head of K-block S-1, then wait
+  // for K-block 0
 #pragma unroll
-  for (int s = 0; s < S; ++s) issue(min(s, KB - 1), s);
-  wait_vm<(S - 1) * T::DMA_PER_STAGE>();
+  for (int x = 0; x < S - 1; ++x)
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue_one(min(x, KB - 1), x, d);
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (dma_slot(d) < POST) issue_one(min(S - 1, KB - 1), S - 1, d);
+  wait_vm<(S - 2) * D + N_HEAD>();
   block_barrier();
 
-  i32x8 fa[TM], fb;
+  // B fragments live in a ring of three: column j+2 is read while column j
+  // computes. A fragments are held for the whole K-block.
+  i32x8 fa[TM], fbr[3];
   float s_lo[TM], s_hi[TM];
-  auto load_scales = [&](const lds_u8* st, int kb) {
+  // activation scales of this lane's rows and the weight scale(s) of the
+  // wave's columns, all from the stage's LDS copy (sb at a wave-uniform address)
+  auto scale_read = [&](const lds_u8* st, float (&a)[TM], float& b0, float& b1) {
     lds_f32* sas = (lds_f32*)(st + T::A_BYTES + T::B_BYTES);
-    const float b0 = sbg[uniform(nb_lo * KB + kb)];
-    const float b1 = sbg[uniform(nb_hi * KB + kb)];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = sas[wm * WM + i * 16 + lr];
+    b0 = sas[BM + nb_lo - nb_tile];
+    b1 = sas[BM + nb_hi - nb_tile];
+  };
+  auto set_scales = [&](const float (&a)[TM], float b0, float b1) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const float a = sas[wm * WM + i * 16 + lr];
-      s_lo[i] = a * b0;
-      s_hi[i] = T::STRADDLE ? a * b1 : 0.f;
+      s_lo[i] = a[i] * b0;
+      s_hi[i] = T::STRADDLE ? a[i] * b1 : 0.f;
     }
   };
 #pragma unroll
   for (int i = 0; i < TM; ++i) fa[i] = frag_read(lds, wm * WM + i * 16 + lr, lq);
-  fb = frag_read(lds + T::A_BYTES, wn * WN + lr, lq);
-  load_scales(lds, 0);
+  fbr[0] = frag_read(lds + T::A_BYTES, wn * WN + lr, lq);
+  if (TN > 1) fbr[1] = frag_read(lds + T::A_BYTES, wn * WN + 16 + lr, lq);
+  {
+    float a0[TM], b0, b1;
+    scale_read(lds, a0, b0, b1);
+    set_scales(a0, b0, b1);
+  }
 
   // One K-block: TM x TN MFMAs in column order. Step u issues MFMA u and then
-  // promotes MFMA u-1 (already complete by then), so the FMAs run under the
-  // next MFMA. Column j+1's B fragment is read at the start of column j. The
-  // barrier precedes the last column; after it the next stage's A fragments
-  // replace each fa[i] as soon as its last MFMA has been issued. ISSUE = false is
-  // the tail (no DMA left to issue; wait for everything outstanding).
+  // promotes MFMA u-1 (complete by then), so the FMAs run under the next
+  // MFMA. The barrier sits before column JB = TN-2, when every read of the
+  // current stage has been issued; after it the next stage's first two B
+  // fragments and its scales are read into free ring slots, and each fa[i] is
+  // replaced by the next stage's fragment right after its last MFMA.
   int stage = 0;
-  auto kblock = [&](int kb, bool ISSUE) {
+  for (int kb = 0; kb < KB; ++kb) {
     const int nstage = stage + 1 == S ? 0 : stage + 1;
+    const int pstage = stage == 0 ? S - 1 : stage - 1;   // stage of K-block kb+S-1
+    const int kb_head = min(kb + S, KB - 1), kb_tail = min(kb + S - 1, KB - 1);
     const lds_u8* cur = lds + stage * T::STAGE_BYTES;
     const lds_u8* nxt = lds + nstage * T::STAGE_BYTES;
     f32x4 part[2];
-    i32x8 fb_next;
+    float sa_next[TM], sb_next0 = 0.f, sb_next1 = 0.f;
 #pragma unroll
-    for (int u = 0; u < TM * TN; ++u) {
+    for (int u = 0; u < STEPS; ++u) {
       const int j = u / TM, i = u % TM;
-      if (j == TN - 1 && i == 0) {
-        // every read of the current stage has been issued: publish the next
-        // stage and recycle this one
+      if (u == PRE) {
         wait_lgkm0();
-        if (ISSUE) wait_vm<(S - 2) * T::DMA_PER_STAGE>();
-        else wait_vm<0>();
+        wait_vm<(S - 2) * D>();
         block_barrier();
-        if (ISSUE) issue(kb + S, stage);
-        fb_next = frag_read(nxt + T::A_BYTES, wn * WN + lr, lq);
+        scale_read(nxt, sa_next, sb_next0, sb_next1);
       }
-      part[u & 1] = mfma_e4m3(fb, fa[i]);
-      if (i == 0 && j + 1 < TN) fb_next = frag_read(cur + T::A_BYTES, wn * WN + (j + 1) * 16 + lr, lq);
+      part[u & 1] = mfma_e4m3(fbr[j % 3], fa[i]);
+      if (i == 0) {
+        // column j+2 of this stage, or (past the end) column j+2-TN of the next
+        const int jn = j + 2;
+        if (jn < TN) fbr[jn % 3] = frag_read(cur + T::A_BYTES, wn * WN + jn * 16 + lr, lq);
+        else fbr[jn % 3] = frag_read(nxt + T::A_BYTES, wn * WN + (jn - TN) * 16 + lr, lq);
+      }
       if (j == TN - 1) fa[i] = frag_read(nxt, wm * WM + i * 16 + lr, lq);
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (u >= PRE && dma_slot(d) == u - PRE) issue_one(kb_head, stage, d);
+        if (u < PRE && dma_slot(d) == POST + u) issue_one(kb_tail, pstage, d);
+      }
       if (u > 0) {
         const int pj = (u - 1) / TM, pi = (u - 1) % TM;
         const float s = (!T::STRADDLE || pj < j_switch) ? s_lo[pi] : s_hi[pi];
         promote(acc[pi][pj], part[(u - 1) & 1], s);
       }
-      if (i == TM - 1) fb = fb_next;
       step_fence();
     }
     {
-      constexpr int u = TM * TN - 1;
       const float s = (!T::STRADDLE || TN - 1 < j_switch) ? s_lo[TM - 1] : s_hi[TM - 1];
-      promote(acc[TM - 1][TN - 1], part[u & 1], s);
+      promote(acc[TM - 1][TN - 1], part[(STEPS - 1) & 1], s);
     }
-    load_scales(nxt, min(kb + 1, KB - 1));
+    // the next stage's first columns sit in ring slots TN % 3 and (TN+1) % 3
+    if (TN % 3 != 0) {
+      const i32x8 c0 = fbr[TN % 3];
+      const i32x8 c1 = fbr[(TN + 1) % 3];
+      fbr[0] = c0;
+      fbr[1] = c1;
+    }
+    set_scales(sa_next, sb_next0, sb_next1);
     stage = nstage;
-  };
+  }
 
-  int kb = 0;
-  for (; kb + S < KB; ++kb) kblock(kb, true);
-  for (; kb < KB; ++kb) kblock(kb, false);
-
-  // ---- epilogue: bf16 RNE, one 8-byte store per lane per sub-tile
-  if (!wave_active) return;
+  // ---- epilogue: bf16 RNE, staged through LDS so that every global store is
+  // a full 16-byte piece of a contiguous output row
+  wait_vm<0>();          // the clamped tail DMAs must land before LDS is reused
+  wait_lgkm0();
+  block_barrier();
+  constexpr int ROWB = T::ROWB;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * WM + i * 16 + lr;
-    bool ok = m < rows_valid;
-    if (LAYOUT == kContiguous && ok) ok = p.m_indices[m] == g;
-    if (!ok) continue;
+    const int ml = wm * WM + i * 16 + lr;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * WN + j * 16 + 4 * lq;
-      if (n >= p.N) continue;
+      const int nl = wn * WN + j * 16 + 4 * lq;
       const uint32_t lo = bf16_rne_bits(acc[i][j][0]) | (bf16_rne_bits(acc[i][j][1]) << 16);
       const uint32_t hi = bf16_rne_bits(acc[i][j][2]) | (bf16_rne_bits(acc[i][j][3]) << 16);
-      *(uint2*)(Dg + (size_t)m * p.N + n) = make_uint2(lo, hi);
+      *(__attribute__((address_space(3))) u32x2*)(lds + ml * ROWB + nl * 2) = u32x2{lo, hi};
+    }
+  }
+  wait_lgkm0();
+  block_barrier();
+  constexpr int CPR = BN * 2 / 16;   // 16-byte pieces per output row
+#pragma unroll 4
+  for (int c = t; c < BM * CPR; c += T::THREADS) {
+    const int row = c / CPR, cc = c - row * CPR;
+    const int m = m0 + row, n = n0 + cc * 8;
+    bool ok = m < rows_valid && n < p.N;
+    if (LAYOUT == kContiguous && ok) ok = p.m_indices[m] == g;
+    if (ok) {
+      const i32x4 v = *(const __attribute__((address_space(3))) i32x4*)(lds + row * ROWB + cc * 16);
+      *(i32x4*)(Dg + (size_t)m * p.N + n) = v;
     }
   }
 }
