@@ -35,6 +35,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 256 * 2.4e9 * 8192 / 1e12    # 5033: 256 CUs x 2.4 GHz x 8192 FLOP/clk/CU
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_02_amd", "csrc", f)
+                  for f in ("fg_kernel.hpp", "fg_host.hip")]
 PEAK_HBM_GBPS = 8000.0                          # HBM3E, 8 TB/s
 MALL_BYTES = 256 << 20
 HEADLINE = "dense_skinny"
@@ -52,6 +55,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle baseline sample")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="summarise rocprofv3 output under DIR (trace/, fetch/, write/ subfolders "
+                         "from --kernel-trace --stats, --pmc FETCH_SIZE, --pmc WRITE_SIZE runs of "
+                         "this script with --calibrate-copy-mb) and update profiles/traffic.json")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="also run device-to-device copies of this many MiB (a kernel of known "
+                         "traffic, used to scale the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -224,8 +234,122 @@ def cpu_baseline(name, target_s):
                       f"host cpus {len(os.sched_getaffinity(0))}"}
 
 
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the kernel sources as they are now; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    entry = t.get("workloads", {}).get(workload)
+    return entry.get("hbm_bytes_per_launch") if entry else None
+
+
+def copy_calibration(mb, torch):
+    """Device-to-device copies of a known size: FETCH_SIZE / WRITE_SIZE of
+    these dispatches give the counters' scale (bytes per counted KiB)."""
+    n = mb << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    evict = torch.empty_like(src)
+    src.fill_(1)
+    evict.fill_(2)     # pushes src out of the 256 MB last-level cache
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst, evict
+    torch.cuda.empty_cache()
+    return n
+
+
+def summarize_profile(root, workload, copy_mb):
+    """Kernel-trace statistics and HBM traffic of the GEMM kernel from rocprofv3
+    CSV output. The FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) are
+    scaled by the ratio of known to counted bytes of the calibration copy."""
+    import csv
+    import glob
+
+    def rows(sub, name):
+        out = []
+        for f in glob.glob(os.path.join(root, sub, "**", name), recursive=True):
+            with open(f) as fh:
+                out += list(csv.DictReader(fh))
+        return out
+
+    stats = rows("trace", "*kernel_stats.csv")
+    gemm = [r for r in stats if "fp8_bs_gemm" in r["Name"]]
+    res = {"workload": workload, "kernels": {}}
+    for r in gemm:
+        res["kernels"][r["Name"]] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                                     "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+
+    def counter(sub, cname):
+        vals = {}
+        for r in rows(sub, "*counter_collection.csv"):
+            if r["Counter_Name"] != cname:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = counter("fetch", "FETCH_SIZE"), counter("write", "WRITE_SIZE")
+    known_kib = copy_mb * 1024.0
+
+    def copy_factor(vals):
+        best = None
+        for name, v in vals.items():
+            if "fp8_bs_gemm" in name or "quant_" in name:
+                continue
+            m = max(v)   # the copy is the largest non-GEMM dispatch
+            if best is None or m > best:
+                best = m
+        return known_kib / best if best else None
+
+    ff, wf = copy_factor(fetch), copy_factor(write)
+    gk = [k for k in fetch if "fp8_bs_gemm" in k]
+    if gk and ff and wf:
+        k = gk[0]
+        f_kib = sum(fetch[k]) / len(fetch[k])
+        w_kib = sum(write.get(k, [0.0])) / max(1, len(write.get(k, [])))
+        res.update(kernel=k, fetch_kib=f_kib, write_kib=w_kib, fetch_scale=ff, write_scale=wf,
+                   hbm_bytes_per_launch=(f_kib * ff + w_kib * wf) * 1024.0)
+    print(json.dumps(res, indent=1))
+    if "hbm_bytes_per_launch" in res:
+        try:
+            with open(TRAFFIC_FILE) as fh:
+                t = json.load(fh)
+        except (OSError, ValueError):
+            t = {}
+        if t.get("source_hash") != kernel_source_hash():
+            t = {"source_hash": kernel_source_hash(), "workloads": {}}
+        t["workloads"][workload] = {"kernel": res["kernel"],
+                                    "hbm_bytes_per_launch": round(res["hbm_bytes_per_launch"]),
+                                    "fetch_kib": round(res["fetch_kib"], 1),
+                                    "write_kib": round(res["write_kib"], 1),
+                                    "fetch_scale": round(res["fetch_scale"], 4),
+                                    "write_scale": round(res["write_scale"], 4)}
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(t, fh, indent=1)
+    return res
+
+
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload, args.calibrate_copy_mb or 256)
+        return
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU path is not built)", file=sys.stderr)
@@ -268,6 +392,10 @@ def main():
             per[name] = summarize(r)
             del r
             torch.cuda.empty_cache()
+
+    if args.calibrate_copy_mb:
+        copy_calibration(args.calibrate_copy_mb, torch)
+    roof["traffic"] = measured_traffic(args.workload)
 
     cpu = None
     if not args.no_cpu_baseline:
