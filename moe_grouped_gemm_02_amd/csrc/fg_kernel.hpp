@@ -312,39 +312,68 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- DMA schedule. K-block x lands in stage x % S. Its stage is freed at
-  // the barrier of K-block x-S and must be complete at the barrier of K-block
-  // x-1. With S >= 3 its instructions are spread one per pipeline step over
-  // the K-block after the freeing barrier ("head" after that barrier, "tail"
-  // before the next one), leaving a further full K-block for the loads to
-  // land; with S = 2 they are spread over the steps right after the freeing
-  // barrier. Spreading keeps the MFMA pipe fed instead of stalling every wave
-  // on a burst of DMA issue. K-block indices past the end are clamped (those
-  // repeat loads hit L2), which keeps every wave's DMA count a compile-time
-  // constant for the vmcnt waits.
+  // ---- DMA schedule. K-block x lands in stage x % S.
+  //
+  // S >= 3: x's stage is freed at the barrier of K-block x-S and must be
+  // complete at the barrier of K-block x-1. Its instructions are spread one per
+  // pipeline step over the K-block after the freeing barrier ("head" after that
+  // barrier, "tail" before the next one), leaving a further full K-block for
+  // the loads to land.
+  //
+  // S == 2: each K-block takes two barriers. The A fragments are held in
+  // registers for the whole K-block, so a stage's A half is free once column 0
+  // has consumed them: a first barrier after column 0 releases it, and the A
+  // half of K-block kb+2 is spread over the rest of K-block kb (almost two
+  // K-blocks to land). The B half (and the scales) is freed by the main
+  // barrier before column TN-2 and spread over the last two columns.
+  //
+  // Spreading keeps the MFMA pipe fed instead of stalling every wave on a
+  // burst of DMA issue. K-block indices past the end are clamped (those repeat
+  // loads hit L2), which keeps every wave's DMA count a compile-time constant
+  // for the vmcnt waits.
   constexpr int STEPS = TM * TN;
-  constexpr int JB = TN - 2;          // the barrier precedes sub-tile column JB
-  constexpr int PRE = JB * TM;        // pipeline steps before the barrier
+  constexpr int JB = TN - 2;          // the main barrier precedes sub-tile column JB
+  constexpr int PRE = JB * TM;        // pipeline steps before it
   constexpr int POST = STEPS - PRE;   // pipeline steps after it
   constexpr int D = T::DMA_PER_STAGE;
-  auto dma_slot = [](int d) constexpr { return S >= 3 ? d * STEPS / D : d * POST / D; };
-  constexpr int N_HEAD = [] {
+  constexpr bool SPLIT = S == 2;
+  constexpr int NA = T::A_INSTR, NBS = D - T::A_INSTR;
+  // pipeline step at which DMA instruction d is issued (S >= 3: position in the
+  // head/tail window of STEPS steps that starts after the freeing barrier)
+  auto dma_slot = [](int d) constexpr {
+    if (SPLIT) return d < NA ? TM + d * (STEPS - TM) / NA : PRE + (d - NA) * POST / NBS;
+    return d * STEPS / D;
+  };
+  constexpr int N_HEAD = [] {   // S >= 3: instructions issued after the freeing barrier
     int n = 0;
-    for (int d = 0; d < D; ++d) n += (S >= 3 ? d * STEPS / D : d * POST / D) < POST;
+    for (int d = 0; d < D; ++d) n += d * STEPS / D < POST;
     return n;
   }();
-  static_assert((S - 2) * D + N_HEAD < 64, "vmcnt counter range");
+  constexpr int N_EARLY = [] {  // S == 2: A instructions issued before the main barrier
+    int n = 0;
+    if (SPLIT)
+      for (int d = 0; d < NA; ++d) n += TM + d * (STEPS - TM) / NA < PRE;
+    return n;
+  }();
+  static_assert((S - 2) * D + N_HEAD < 64 && D + N_EARLY < 64, "vmcnt counter range");
 
-  // ---- prologue: K-blocks 0 .. S-2 and the head of K-block S-1, then wait
-  // for K-block 0
+  // ---- prologue: wait for K-block 0 with the later ones in flight
+  //   S >= 3: K-blocks 1 .. S-2 and the head of K-block S-1
+  //   S == 2: K-block 1
 #pragma unroll
   for (int x = 0; x < S - 1; ++x)
 #pragma unroll
     for (int d = 0; d < D; ++d) issue_one(min(x, KB - 1), x, d);
+  if (SPLIT) {
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (dma_slot(d) < POST) issue_one(min(S - 1, KB - 1), S - 1, d);
-  wait_vm<(S - 2) * D + N_HEAD>();
+    for (int d = 0; d < D; ++d) issue_one(min(1, KB - 1), 1, d);
+    wait_vm<D>();
+  } else {
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (dma_slot(d) < POST) issue_one(min(S - 1, KB - 1), S - 1, d);
+    wait_vm<(S - 2) * D + N_HEAD>();
+  }
   block_barrier();
 
   // B fragments live in a ring of three: column j+2 is read while column j
@@ -395,9 +424,12 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
 #pragma unroll
     for (int u = 0; u < STEPS; ++u) {
       const int j = u / TM, i = u % TM;
+      if (SPLIT && u == TM && TM < PRE) block_barrier();   // A half of this stage is free
       if (u == PRE) {
+        // every read of the current stage has been issued; the next stage (and,
+        // for S == 2, every DMA older than this K-block's early A loads) is in
         wait_lgkm0();
-        wait_vm<(S - 2) * D>();
+        wait_vm<(S - 2) * D + N_EARLY>();
         block_barrier();
         scale_read(nxt, sa_next, sb_next0, sb_next1);
       }
@@ -411,8 +443,12 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
       if (j == TN - 1) fa[i] = frag_read(nxt, wm * WM + i * 16 + lr, lq);
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        if (u >= PRE && dma_slot(d) == u - PRE) issue_one(kb_head, stage, d);
-        if (u < PRE && dma_slot(d) == POST + u) issue_one(kb_tail, pstage, d);
+        if (SPLIT) {
+          if (dma_slot(d) == u) issue_one(kb_head, stage, d);   // K-block kb+2 into this stage
+        } else {
+          if (u >= PRE && dma_slot(d) == u - PRE) issue_one(kb_head, stage, d);
+          if (u < PRE && dma_slot(d) == POST + u) issue_one(kb_tail, pstage, d);
+        }
       }
       if (u > 0) {
         const int pj = (u - 1) / TM, pi = (u - 1) % TM;
