@@ -46,6 +46,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fg {
 
 typedef int   i32x4 __attribute__((ext_vector_type(4)));
@@ -76,39 +79,98 @@ struct Params {
   int tiles_m, tiles_n;   // tile grid of one group
 };
 
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
+
 // Compile-time tile configuration.
 //   BM x BN   output tile per workgroup
 //   WGM x WGN waves per workgroup (each wave owns a (BM/WGM) x (BN/WGN) block)
 //   STAGES    depth of the LDS ring
 //   STRADDLE  a wave's columns may span two 128-wide scale blocks of B
-template <int BM_, int BN_, int WGM_, int WGN_, int STAGES_, bool STRADDLE_>
+//   PD        B fragments are read PD sub-tile columns ahead of their MFMAs
+//             (a register ring of PD+1 fragments)
+//   FA2       the next K-block's A fragments are read into a second register
+//             set right after the barrier instead of after each one's last use
+//   PL        each MFMA's partial is promoted PL MFMAs after it was issued
+//             (a ring of PL+1 partials, slot = MFMA number modulo PL+1)
+template <int BM_, int BN_, int WGM_, int WGN_, int STAGES_, bool STRADDLE_, int PD_ = 2,
+          bool FA2_ = false, int PL_ = 1>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, STAGES = STAGES_;
   static constexpr bool STRADDLE = STRADDLE_;
+  static constexpr int PD = PD_, RING = PD_ + 1;
+  static constexpr bool FA2 = FA2_;
+  static constexpr int PL = PL_, PARTS = PL_ + 1;
   static constexpr int W = WGM * WGN;
   static constexpr int THREADS = 64 * W;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int TM = WM / 16, TN = WN / 16;
-  // DMA instructions per wave per stage; padding slots load a clamped row.
+  // DMA instructions per wave per stage (16 bytes per lane); padding slots
+  // load a clamped row.
   static constexpr int A_INSTR = (BM * 8 + 64 * W - 1) / (64 * W);
   static constexpr int B_INSTR = (BN * 8 + 64 * W - 1) / (64 * W);
-  static constexpr int SB_SLOTS = 4;   // weight scales of the tile's (up to 3) 128-column blocks
-  static constexpr int SA_INSTR = (BM + SB_SLOTS + 64 * W - 1) / (64 * W);
+  // scale DMAs (4 bytes per lane): one per 64 activation rows plus one for
+  // the weight scales of the tile's (up to 3) 128-column blocks, dealt
+  // round-robin to the waves; a wave with a spare slot repeats a load
+  static constexpr int SC_LOADS = BM / 64 + 1;
+  static constexpr int SC_INSTR = (SC_LOADS + W - 1) / W;
   static constexpr int A_BYTES = A_INSTR * W * 1024;
   static constexpr int B_BYTES = B_INSTR * W * 1024;
-  static constexpr int SA_BYTES = SA_INSTR * W * 256;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES;
-  static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int SC_BYTES = BM * 4 + 256;
+  // LDS ring: the scale blocks of all stages, then the A tiles, then the B
+  // tiles (scale reads then always fall within the first 64 KB)
+  static constexpr int SC_BASE = 0;
+  static constexpr int A_BASE = STAGES * SC_BYTES;
+  static constexpr int B_BASE = A_BASE + STAGES * A_BYTES;
+  static constexpr int RING_BYTES = B_BASE + STAGES * B_BYTES;
   static constexpr int ROWB = BN * 2 + 16;   // staged bf16 output row (+16 B against bank conflicts)
   static constexpr int LDS_BYTES = RING_BYTES > BM * ROWB ? RING_BYTES : BM * ROWB;
-  static constexpr int DMA_PER_STAGE = A_INSTR + B_INSTR + SA_INSTR;
+  static constexpr int DMA_PER_STAGE = A_INSTR + B_INSTR + SC_INSTR;
+  // K-blocks per main-loop iteration: every per-K-block choice (ring stage,
+  // B-ring slots, A-fragment set, scale set) repeats with this period, so each
+  // copy of the K-block body works with compile-time registers and offsets
+  static constexpr int UNROLL =
+      lcm_c(lcm_c(lcm_c(STAGES, RING / gcd_c(TN, RING)), PARTS / gcd_c(TM * TN, PARTS)), 2);
   static_assert(WM % 16 == 0 && WN % 16 == 0 && TM >= 1 && TN >= 1, "wave tile must be 16-aligned");
   static_assert(BM % WGM == 0 && BN % WGN == 0, "waves must split the tile evenly");
+  static_assert(BM % 64 == 0, "activation scales are loaded 64 rows at a time");
   static_assert(STAGES >= 2, "need at least double buffering");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
   static_assert(WN <= 128, "a wave's columns may touch at most two scale blocks");
-  static_assert(TN >= 2, "the B-fragment ring needs at least two sub-tile columns per wave");
+  static_assert(PD >= 1 && PD <= TN - 1, "prefetch distance must leave the barrier inside the K-block");
+  static_assert(PL >= 1 && PL < TM * TN, "promotion lag must stay within one K-block");
   static_assert(STRADDLE || 128 % WN == 0, "non-straddling waves must tile the 128-wide scale blocks");
+};
+
+// Pipeline-step schedule of one K-block (see the kernel for its meaning).
+template <class T>
+struct Sched {
+  static constexpr int STEPS = T::TM * T::TN;
+  static constexpr int JB = T::TN - T::PD;     // the main barrier precedes sub-tile column JB
+  static constexpr int PRE = JB * T::TM;       // pipeline steps before it
+  static constexpr int POST = STEPS - PRE;     // pipeline steps after it
+  static constexpr int D = T::DMA_PER_STAGE;
+  static constexpr bool SPLIT = T::STAGES == 2;
+  static constexpr int NA = T::A_INSTR, NBS = D - T::A_INSTR;
+  // pipeline step at which DMA instruction d is issued (S >= 3: position in the
+  // head/tail window of STEPS steps that starts after the freeing barrier)
+  static constexpr int slot(int d) {
+    if (SPLIT) return d < NA ? T::TM + d * (STEPS - T::TM) / NA : PRE + (d - NA) * POST / NBS;
+    return d * STEPS / D;
+  }
+  // S >= 3: instructions issued after the freeing barrier
+  static constexpr int n_head() {
+    int n = 0;
+    for (int d = 0; d < D; ++d) n += slot(d) < POST;
+    return n;
+  }
+  // S == 2: A instructions issued before the main barrier
+  static constexpr int n_early() {
+    int n = 0;
+    if (SPLIT)
+      for (int d = 0; d < NA; ++d) n += slot(d) < PRE;
+    return n;
+  }
 };
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
@@ -141,23 +203,32 @@ __device__ __forceinline__ void block_barrier() {
 // host+device, and a gfx950 builtin inside one would make the host-side
 // instantiation of the kernel (its launch stub) silently fail.
 //
-// The LDS-DMA loads are issued through inline asm. When the compiler sees an
-// LDS-DMA in flight it can no longer count LDS reads precisely and waits for
-// all of them (lgkmcnt(0)) before every fragment use; hidden from it, the DMA
-// is tracked only by this kernel's explicit vmcnt waits, and the compiler's
-// lgkmcnt waits cover exactly the fragment reads. M0 holds the wave-uniform
+// The LDS-DMA loads (buffer_load ... lds) are issued through inline asm. When
+// the compiler sees an LDS-DMA in flight it can no longer count LDS reads
+// precisely and waits for all of them (lgkmcnt(0)) before every fragment use;
+// hidden from it, the DMA is tracked only by this kernel's explicit vmcnt
+// waits, and the compiler's lgkmcnt waits cover exactly the fragment reads.
+// Each operand is addressed through a buffer resource (base and byte size; the
+// hardware range check keeps every load inside the operand), a loop-invariant
+// per-lane offset and one scalar offset per K-block. M0 holds the wave-uniform
 // LDS destination; one wait state separates its write from the DMA.
-__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, lds_u8* dst) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"((uint32_t)(uintptr_t)dst) : "memory");
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)bytes, 0x20000};
 }
-__device__ __forceinline__ void dma4(const uint8_t* addr, lds_u8* dst) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(addr), "s"((uint32_t)(uintptr_t)dst) : "memory");
+template <int IMM>
+__device__ __forceinline__ void dma16(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t lds_at) {
+  asm volatile("s_add_u32 m0, %3, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rs), "s"(soff), "s"(lds_at), "n"(IMM) : "memory", "scc");
+}
+template <int IMM>
+__device__ __forceinline__ void dma4(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t lds_at) {
+  asm volatile("s_add_u32 m0, %3, %4\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rs), "s"(soff), "s"(lds_at), "n"(IMM) : "memory", "scc");
 }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 // Keep one pipeline step's order -- the MFMA first, then its LDS reads, then
-// the VALU promotion of the previous partial -- and let nothing cross steps.
+// the VALU promotion of an earlier partial -- and let nothing cross steps.
 __device__ __forceinline__ void step_fence() {
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
@@ -165,10 +236,53 @@ __device__ __forceinline__ void step_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ i32x8 frag_read(const lds_u8* tile, int row, int lq) {
-  const i32x4 lo = *(const __attribute__((address_space(3))) i32x4*)(tile + swz(row, lq));
-  const i32x4 hi = *(const __attribute__((address_space(3))) i32x4*)(tile + swz(row, lq + 4));
-  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+// A per-lane LDS byte address with one copy per 64 KB window, hidden from the
+// compiler so that an access at base + OFF (OFF a compile-time constant)
+// becomes one DS instruction with the 16-bit immediate OFF % 65536.
+template <int NWIN>
+struct LdsAddr {
+  uint32_t w[NWIN];
+  __device__ __forceinline__ void init(uint32_t a) {
+#pragma unroll
+    for (int k = 0; k < NWIN; ++k) {
+      w[k] = a + (uint32_t)k * 65536u;
+      asm("" : "+v"(w[k]));
+    }
+  }
+  template <int OFF>
+  __device__ __forceinline__ const lds_u8* at() const {
+    static_assert(OFF >= 0 && (OFF >> 16) < NWIN, "LDS window");
+    return (const lds_u8*)(size_t)w[OFF >> 16] + (OFF & 0xffff);
+  }
+};
+template <int OFF, int NWIN>
+__device__ __forceinline__ i32x8 frag_at(const LdsAddr<NWIN>& lo, const LdsAddr<NWIN>& hi) {
+  const i32x4 a = *(const __attribute__((address_space(3))) i32x4*)lo.template at<OFF>();
+  const i32x4 b = *(const __attribute__((address_space(3))) i32x4*)hi.template at<OFF>();
+  return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+template <int OFF, int NWIN>
+__device__ __forceinline__ float f32_at(const LdsAddr<NWIN>& b) {
+  return *(const lds_f32*)b.template at<OFF>();
+}
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>)
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <class F, int... I>
+__device__ __forceinline__ bool static_any_impl(F&& f, std::integer_sequence<int, I...>) {
+  return (f(std::integral_constant<int, I>{}) || ...);
+}
+// f(0) || f(1) || ... || f(N-1), evaluated in order, stopping at the first true
+template <int N, class F>
+__device__ __forceinline__ bool static_any(F&& f) {
+  return static_any_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ f32x4 mfma_e4m3(const i32x8& b_rows, const i32x8& a_rows) {
@@ -185,7 +299,8 @@ __device__ __forceinline__ void promote(f32x4& acc, const f32x4& part, float s) 
 template <int LAYOUT, class T>
 __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   constexpr int BM = T::BM, BN = T::BN, W = T::W, WM = T::WM, WN = T::WN;
-  constexpr int TM = T::TM, TN = T::TN, S = T::STAGES;
+  constexpr int TM = T::TM, TN = T::TN, S = T::STAGES, PD = T::PD, R = T::RING;
+  constexpr int PL = T::PL, P = T::PARTS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
   __shared__ int s_group;
   lds_u8* const lds = (lds_u8*)smem;
@@ -252,11 +367,21 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   const float* sbg = p.sb + (LAYOUT != kDense ? (size_t)g * (p.N / 128) * KB : 0);
   uint16_t* Dg = p.D + (LAYOUT == kMasked ? (size_t)g * M * p.N : 0);
 
-  // ---- per-lane DMA sources (byte offsets within one K-block column).
-  // Slot s of a region is the 16-byte LDS chunk s; it holds row s/8, chunk
-  // position s%8, i.e. global chunk (s%8) ^ (row%8). Rows past the tile
-  // (padding slots) and past the matrix are clamped to a valid row.
-  uint32_t a_off[T::A_INSTR], b_off[T::B_INSTR], sa_off[T::SA_INSTR];
+  const i32x4 rsA = buffer_rsrc(Ag, (uint32_t)M * (uint32_t)K);
+  const i32x4 rsB = buffer_rsrc(Bg, (uint32_t)p.N * (uint32_t)K);
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- DMA sources: a buffer resource per operand and per-lane byte offsets
+  // within one K-block column. Slot s of a tile region is the 16-byte LDS
+  // chunk s; it holds row s/8, chunk position s%8, i.e. global chunk
+  // (s%8) ^ (row%8). Rows past the tile (padding slots) and past the matrix
+  // are clamped to a valid row.
+  uint32_t a_off[T::A_INSTR], b_off[T::B_INSTR];
 #pragma unroll
   for (int q = 0; q < T::A_INSTR; ++q) {
     const int slot = (q * W + wave) * 64 + lane;
@@ -271,31 +396,50 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
     const int n = min(n0 + min(row, BN - 1), p.N - 1);
     b_off[q] = (uint32_t)n * (uint32_t)K + chunk * 16;
   }
-  // scale slots: [0, BM) activation rows, [BM, BM+4) weight blocks from the
-  // tile's first 128-column block on (clamped), the rest duplicate a row
+  // Scale loads: load i = q*W + wave brings activation rows [64i, 64i+64)
+  // (i < BM/64) or the weight scales of the tile's 128-column blocks
+  // (i == BM/64, clamped); a wave without a load of its own repeats load 0.
   const int nb_tile = n0 >> 7;
-  bool sa_is_sb[T::SA_INSTR];
+  const i32x4 rsSA = buffer_rsrc(sag, (uint32_t)KB * (uint32_t)M * 4u);
+  const i32x4 rsSB = buffer_rsrc(sbg, (uint32_t)(p.N / 128) * (uint32_t)KB * 4u);
+  i32x4 rsS[T::SC_INSTR];
+  uint32_t sc_off[T::SC_INSTR], sc_stride[T::SC_INSTR], sc_dst[T::SC_INSTR];
 #pragma unroll
-  for (int q = 0; q < T::SA_INSTR; ++q) {
-    const int idx = (q * W + wave) * 64 + lane;
-    sa_is_sb[q] = idx >= BM && idx < BM + T::SB_SLOTS;
-    sa_off[q] = sa_is_sb[q] ? (uint32_t)min(nb_tile + idx - BM, p.N / 128 - 1) * (uint32_t)KB * 4u
-                            : (uint32_t)min(m0 + min(idx, BM - 1), M - 1) * 4u;
+  for (int q = 0; q < T::SC_INSTR; ++q) {
+    int i = q * W + wave;
+    if (i >= T::SC_LOADS) i = 0;
+    const bool is_b = i == BM / 64;
+    rsS[q] = is_b ? rsSB : rsSA;
+    sc_stride[q] = is_b ? 4u : (uint32_t)M * 4u;
+    sc_dst[q] = lds_addr + T::SC_BASE + (is_b ? BM * 4 : i * 256);
+    sc_off[q] = is_b ? (uint32_t)min(nb_tile + lane, p.N / 128 - 1) * (uint32_t)KB * 4u
+                     : (uint32_t)min(m0 + i * 64 + lane, M - 1) * 4u;
   }
+  const uint32_t wave_at = lds_addr + wave * 1024;   // this wave's 1 KB DMA slot in a tile region
 
-  // One DMA instruction d (0 .. DMA_PER_STAGE-1) of K-block kb into a stage:
-  // A chunks first, then B chunks, then the scale slots.
-  auto issue_one = [&](int kb, int stage, int d) {
-    lds_u8* const base = lds + stage * T::STAGE_BYTES;
-    if (d < T::A_INSTR) {
-      dma16(Ag + (size_t)kb * kKBlock, a_off[d], base + (d * W + wave) * 1024);
-    } else if (d < T::A_INSTR + T::B_INSTR) {
-      const int q = d - T::A_INSTR;
-      dma16(Bg + (size_t)kb * kKBlock, b_off[q], base + T::A_BYTES + (q * W + wave) * 1024);
+  // scalar offsets of K-block kbd for the tile loads and for each scale load
+  struct Soff {
+    uint32_t ab, sc[T::SC_INSTR];
+  };
+  auto soff_of = [&](int kbd) {
+    Soff o;
+    o.ab = (uint32_t)kbd * (uint32_t)kKBlock;
+#pragma unroll
+    for (int q = 0; q < T::SC_INSTR; ++q) o.sc[q] = (uint32_t)kbd * sc_stride[q];
+    return o;
+  };
+  constexpr int NA = T::A_INSTR, NB = T::B_INSTR;
+  // DMA instruction d (A chunks, then B chunks, then scale loads) of a K-block
+  // into ring stage ST
+  auto issue = [&](auto d_c, auto st_c, const Soff& o) {
+    constexpr int d = decltype(d_c)::value, ST = decltype(st_c)::value;
+    if constexpr (d < NA) {
+      dma16<T::A_BASE + ST * T::A_BYTES + d * W * 1024>(rsA, a_off[d], o.ab, wave_at);
+    } else if constexpr (d < NA + NB) {
+      dma16<T::B_BASE + ST * T::B_BYTES + (d - NA) * W * 1024>(rsB, b_off[d - NA], o.ab, wave_at);
     } else {
-      const int q = d - T::A_INSTR - T::B_INSTR;
-      const uint8_t* const src = sa_is_sb[q] ? (const uint8_t*)(sbg + kb) : (const uint8_t*)(sag + (size_t)kb * M);
-      dma4(src + sa_off[q], base + T::A_BYTES + T::B_BYTES + (q * W + wave) * 256);
+      constexpr int q = d - NA - NB;
+      dma4<ST * T::SC_BYTES>(rsS[q], sc_off[q], o.sc[q], sc_dst[q]);
     }
   };
 
@@ -306,13 +450,32 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   // first sub-tile column whose scale block is nb_hi
   const int j_switch = T::STRADDLE ? uniform(((nb_lo + 1) * 128 - wn0) >> 4) : TN;
 
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ---- per-lane LDS addresses of this wave's fragments and scales. Chunk c
+  // of tile row r sits at r*128 + ((c ^ (r & 7)) << 4); a wave's fragments
+  // start at multiples of 16 rows, so r & 7 == lr & 7 and every fragment is
+  // one of four per-lane bases plus a compile-time offset.
+  constexpr int NWIN = (T::RING_BYTES + 65535) >> 16;
+  LdsAddr<NWIN> aLo, aHi, bLo, bHi, sA, sB0, sB1;
+  {
+    const uint32_t lane_lo = lr * 128 + ((lq ^ (lr & 7)) << 4);
+    const uint32_t lane_hi = lr * 128 + (((lq + 4) ^ (lr & 7)) << 4);
+    aLo.init(lds_addr + wm * WM * 128 + lane_lo);
+    aHi.init(lds_addr + wm * WM * 128 + lane_hi);
+    bLo.init(lds_addr + wn * WN * 128 + lane_lo);
+    bHi.init(lds_addr + wn * WN * 128 + lane_hi);
+    sA.init(lds_addr + (wm * WM + lr) * 4);
+    sB0.init(lds_addr + (BM + nb_lo - nb_tile) * 4);
+    sB1.init(lds_addr + (BM + nb_hi - nb_tile) * 4);
+  }
+  // A fragment i / B fragment j of ring stage ST
+  auto fragA = [&](auto st_c, auto i_c) {
+    return frag_at<T::A_BASE + decltype(st_c)::value * T::A_BYTES + decltype(i_c)::value * 2048>(aLo, aHi);
+  };
+  auto fragB = [&](auto st_c, auto j_c) {
+    return frag_at<T::B_BASE + decltype(st_c)::value * T::B_BYTES + decltype(j_c)::value * 2048>(bLo, bHi);
+  };
 
-  // ---- DMA schedule. K-block x lands in stage x % S.
+  // ---- DMA schedule. K-block x lands in ring stage x % S.
   //
   // S >= 3: x's stage is freed at the barrier of K-block x-S and must be
   // complete at the barrier of K-block x-1. Its instructions are spread one per
@@ -325,152 +488,206 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   // has consumed them: a first barrier after column 0 releases it, and the A
   // half of K-block kb+2 is spread over the rest of K-block kb (almost two
   // K-blocks to land). The B half (and the scales) is freed by the main
-  // barrier before column TN-2 and spread over the last two columns.
+  // barrier before column TN-PD and spread over the last PD columns.
   //
   // Spreading keeps the MFMA pipe fed instead of stalling every wave on a
   // burst of DMA issue. K-block indices past the end are clamped (those repeat
   // loads hit L2), which keeps every wave's DMA count a compile-time constant
   // for the vmcnt waits.
-  constexpr int STEPS = TM * TN;
-  constexpr int JB = TN - 2;          // the main barrier precedes sub-tile column JB
-  constexpr int PRE = JB * TM;        // pipeline steps before it
-  constexpr int POST = STEPS - PRE;   // pipeline steps after it
-  constexpr int D = T::DMA_PER_STAGE;
-  constexpr bool SPLIT = S == 2;
-  constexpr int NA = T::A_INSTR, NBS = D - T::A_INSTR;
-  // pipeline step at which DMA instruction d is issued (S >= 3: position in the
-  // head/tail window of STEPS steps that starts after the freeing barrier)
-  auto dma_slot = [](int d) constexpr {
-    if (SPLIT) return d < NA ? TM + d * (STEPS - TM) / NA : PRE + (d - NA) * POST / NBS;
-    return d * STEPS / D;
-  };
-  constexpr int N_HEAD = [] {   // S >= 3: instructions issued after the freeing barrier
-    int n = 0;
-    for (int d = 0; d < D; ++d) n += d * STEPS / D < POST;
-    return n;
-  }();
-  constexpr int N_EARLY = [] {  // S == 2: A instructions issued before the main barrier
-    int n = 0;
-    if (SPLIT)
-      for (int d = 0; d < NA; ++d) n += TM + d * (STEPS - TM) / NA < PRE;
-    return n;
-  }();
+  using SCH = Sched<T>;
+  constexpr int STEPS = SCH::STEPS, PRE = SCH::PRE, POST = SCH::POST, D = SCH::D;
+  constexpr bool SPLIT = SCH::SPLIT;
+  constexpr int N_HEAD = SCH::n_head(), N_EARLY = SCH::n_early();
   static_assert((S - 2) * D + N_HEAD < 64 && D + N_EARLY < 64, "vmcnt counter range");
 
   // ---- prologue: wait for K-block 0 with the later ones in flight
   //   S >= 3: K-blocks 1 .. S-2 and the head of K-block S-1
   //   S == 2: K-block 1
-#pragma unroll
-  for (int x = 0; x < S - 1; ++x)
-#pragma unroll
-    for (int d = 0; d < D; ++d) issue_one(min(x, KB - 1), x, d);
-  if (SPLIT) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) issue_one(min(1, KB - 1), 1, d);
+  static_for<S - 1>([&](auto x_c) {
+    const Soff o = soff_of(min((int)decltype(x_c)::value, KB - 1));
+    static_for<D>([&](auto d_c) { issue(d_c, x_c, o); });
+  });
+  if constexpr (SPLIT) {
+    const Soff o = soff_of(min(1, KB - 1));
+    static_for<D>([&](auto d_c) { issue(d_c, std::integral_constant<int, 1>{}, o); });
     wait_vm<D>();
   } else {
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-      if (dma_slot(d) < POST) issue_one(min(S - 1, KB - 1), S - 1, d);
+    const Soff o = soff_of(min(S - 1, KB - 1));
+    static_for<D>([&](auto d_c) {
+      if constexpr (SCH::slot(decltype(d_c)::value) < POST) issue(d_c, std::integral_constant<int, S - 1>{}, o);
+    });
     wait_vm<(S - 2) * D + N_HEAD>();
   }
   block_barrier();
 
-  // B fragments live in a ring of three: column j+2 is read while column j
-  // computes. A fragments are held for the whole K-block.
-  i32x8 fa[TM], fbr[3];
-  float s_lo[TM], s_hi[TM];
-  // activation scales of this lane's rows and the weight scale(s) of the
-  // wave's columns, all from the stage's LDS copy (sb at a wave-uniform address)
-  auto scale_read = [&](const lds_u8* st, float (&a)[TM], float& b0, float& b1) {
-    lds_f32* sas = (lds_f32*)(st + T::A_BYTES + T::B_BYTES);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = sas[wm * WM + i * 16 + lr];
-    b0 = sas[BM + nb_lo - nb_tile];
-    b1 = sas[BM + nb_hi - nb_tile];
+  // Register state. B fragments live in a ring of R = PD+1 (column g of the
+  // K-block sequence, counting columns across K-blocks, in slot g % R); column
+  // j+PD is read while column j computes. A fragments are held for the whole
+  // K-block; with FA2 the K-blocks alternate between two sets and the next
+  // K-block's set is read right after the barrier. Scales alternate between
+  // two sets as well: a K-block's own and its predecessor's, which the first
+  // PL steps still need for the carried promotions.
+  i32x8 fbr[R], fa[T::FA2 ? 2 : 1][TM];
+  float sc_lo[2][TM], sc_hi[2][TM];
+  f32x4 part[P];
+  auto scale_read = [&](auto st_c, float (&a)[TM], float& b0, float& b1) {
+    constexpr int ST = decltype(st_c)::value;
+    static_for<TM>([&](auto i_c) {
+      a[decltype(i_c)::value] = f32_at<T::SC_BASE + ST * T::SC_BYTES + decltype(i_c)::value * 64>(sA);
+    });
+    b0 = f32_at<T::SC_BASE + ST * T::SC_BYTES>(sB0);
+    b1 = f32_at<T::SC_BASE + ST * T::SC_BYTES>(sB1);
   };
-  auto set_scales = [&](const float (&a)[TM], float b0, float b1) {
+  auto set_scales = [&](auto set_c, const float (&a)[TM], float b0, float b1) {
+    constexpr int SET = decltype(set_c)::value;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      s_lo[i] = a[i] * b0;
-      s_hi[i] = T::STRADDLE ? a[i] * b1 : 0.f;
+      sc_lo[SET][i] = a[i] * b0;
+      sc_hi[SET][i] = T::STRADDLE ? a[i] * b1 : 0.f;
     }
   };
-#pragma unroll
-  for (int i = 0; i < TM; ++i) fa[i] = frag_read(lds, wm * WM + i * 16 + lr, lq);
-  fbr[0] = frag_read(lds + T::A_BYTES, wn * WN + lr, lq);
-  if (TN > 1) fbr[1] = frag_read(lds + T::A_BYTES, wn * WN + 16 + lr, lq);
-  {
-    float a0[TM], b0, b1;
-    scale_read(lds, a0, b0, b1);
-    set_scales(a0, b0, b1);
-  }
+  // scale of sub-tile (pi, pj) from scale set SET (a value select: selecting
+  // between the two array elements themselves would keep the arrays in memory)
+  auto scale_of = [&](auto set_c, auto pi_c, auto pj_c) {
+    constexpr int SET = decltype(set_c)::value, pi = decltype(pi_c)::value, pj = decltype(pj_c)::value;
+    const float lo = sc_lo[SET][pi];
+    if constexpr (!T::STRADDLE) return lo;
+    const float hi = sc_hi[SET][pi];
+    return pj >= j_switch ? hi : lo;
+  };
 
-  // One K-block: TM x TN MFMAs in column order. Step u issues MFMA u and then
-  // promotes MFMA u-1 (complete by then), so the FMAs run under the next
-  // MFMA. The barrier sits before column JB = TN-2, when every read of the
-  // current stage has been issued; after it the next stage's first two B
-  // fragments and its scales are read into free ring slots, and each fa[i] is
-  // replaced by the next stage's fragment right after its last MFMA.
-  int stage = 0;
-  for (int kb = 0; kb < KB; ++kb) {
-    const int nstage = stage + 1 == S ? 0 : stage + 1;
-    const int pstage = stage == 0 ? S - 1 : stage - 1;   // stage of K-block kb+S-1
-    const int kb_head = min(kb + S, KB - 1), kb_tail = min(kb + S - 1, KB - 1);
-    const lds_u8* cur = lds + stage * T::STAGE_BYTES;
-    const lds_u8* nxt = lds + nstage * T::STAGE_BYTES;
-    f32x4 part[2];
-    float sa_next[TM], sb_next0 = 0.f, sb_next1 = 0.f;
+  // Stage 0's reads are issued in the order in which the loop itself leaves
+  // the next stage's reads in flight (scales, then FA2 ? A, B : B, A). The
+  // compiler places one LDS wait at the loop head that must hold for both the
+  // entry and the back edge; with matching orders it is the steady-state wait
+  // instead of a full drain on every K-block.
+  {
+    using Z = std::integral_constant<int, 0>;
+    float a0[TM], b0, b1;
+    scale_read(Z{}, a0, b0, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (T::FA2) {
+      static_for<TM>([&](auto i_c) {
+        fa[0][decltype(i_c)::value] = fragA(Z{}, i_c);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    static_for<PD>([&](auto c_c) {
+      fbr[decltype(c_c)::value] = fragB(Z{}, c_c);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (!T::FA2) {
+      static_for<TM>([&](auto i_c) {
+        fa[0][decltype(i_c)::value] = fragA(Z{}, i_c);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    set_scales(std::integral_constant<int, 0>{}, a0, b0, b1);
+  }
+  // before K-block 0 nothing is pending: zero partials promoted with zero
+  // scales leave the (zero) accumulators unchanged
 #pragma unroll
-    for (int u = 0; u < STEPS; ++u) {
-      const int j = u / TM, i = u % TM;
-      if (SPLIT && u == TM && TM < PRE) block_barrier();   // A half of this stage is free
-      if (u == PRE) {
+  for (int c = 0; c < P; ++c) part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < TM; ++i) sc_lo[1][i] = sc_hi[1][i] = 0.f;
+
+  // promotion of MFMA u - PL of a K-block with phase PH (for u < PL: MFMA
+  // STEPS + u - PL of the previous K-block, with the previous scale set)
+  auto promote_step = [&](auto ph_c, auto u_c) {
+    constexpr int PH = decltype(ph_c)::value, u = decltype(u_c)::value;
+    constexpr int v = u - PL;
+    constexpr int w = v >= 0 ? v : v + STEPS;
+    constexpr int pj = w / TM, pi = w % TM;
+    constexpr int set = v >= 0 ? (PH & 1) : ((PH + 1) & 1);
+    promote(acc[pi][pj], part[(PH * STEPS + v + T::UNROLL * STEPS) % P],
+            scale_of(std::integral_constant<int, set>{}, std::integral_constant<int, pi>{},
+                     std::integral_constant<int, pj>{}));
+  };
+
+  // One K-block with compile-time phase PH = kb % U: TM x TN MFMAs in column
+  // order. Step u issues MFMA u and then promotes MFMA u-PL. An MFMA's result
+  // arrives well after the next MFMA could issue; waiting PL MFMAs before
+  // reading it keeps the VALU work off the matrix core's critical path even
+  // with a single wave per SIMD. The barrier sits before column JB = TN-PD,
+  // when every read of the current stage has been issued; after it the next
+  // stage's scales, first PD B fragments and (FA2) A fragments are read, or
+  // (otherwise) each fa[i] is replaced right after its last MFMA.
+  int kb = 0;
+  auto kblock = [&](auto ph_c) -> bool {
+    constexpr int PH = decltype(ph_c)::value;
+    constexpr int ST = PH % S, NST = (PH + 1) % S, TST = (PH + S - 1) % S;
+    constexpr int CA = T::FA2 ? (PH & 1) : 0, NA_SET = T::FA2 ? ((PH + 1) & 1) : 0;
+    using CurSt = std::integral_constant<int, ST>;
+    using NxtSt = std::integral_constant<int, NST>;
+    const Soff head = soff_of(min(kb + S, KB - 1));        // K-block kb+S into stage ST
+    const Soff tail = soff_of(min(kb + S - 1, KB - 1));    // K-block kb+S-1 into stage TST (S >= 3)
+    (void)tail;
+    float sa_next[TM], sb_next0 = 0.f, sb_next1 = 0.f;
+    static_for<STEPS>([&](auto u_c) {
+      constexpr int u = decltype(u_c)::value;
+      constexpr int j = u / TM, i = u % TM;
+      if constexpr (SPLIT && u == TM && TM < PRE) block_barrier();   // A half of this stage is free
+      if constexpr (u == PRE) {
         // every read of the current stage has been issued; the next stage (and,
         // for S == 2, every DMA older than this K-block's early A loads) is in
         wait_lgkm0();
         wait_vm<(S - 2) * D + N_EARLY>();
         block_barrier();
-        scale_read(nxt, sa_next, sb_next0, sb_next1);
-      }
-      part[u & 1] = mfma_e4m3(fbr[j % 3], fa[i]);
-      if (i == 0) {
-        // column j+2 of this stage, or (past the end) column j+2-TN of the next
-        const int jn = j + 2;
-        if (jn < TN) fbr[jn % 3] = frag_read(cur + T::A_BYTES, wn * WN + jn * 16 + lr, lq);
-        else fbr[jn % 3] = frag_read(nxt + T::A_BYTES, wn * WN + (jn - TN) * 16 + lr, lq);
-      }
-      if (j == TN - 1) fa[i] = frag_read(nxt, wm * WM + i * 16 + lr, lq);
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        if (SPLIT) {
-          if (dma_slot(d) == u) issue_one(kb_head, stage, d);   // K-block kb+2 into this stage
-        } else {
-          if (u >= PRE && dma_slot(d) == u - PRE) issue_one(kb_head, stage, d);
-          if (u < PRE && dma_slot(d) == POST + u) issue_one(kb_tail, pstage, d);
+        scale_read(NxtSt{}, sa_next, sb_next0, sb_next1);
+        if constexpr (T::FA2) {
+          static_for<TM>([&](auto ii_c) { fa[NA_SET][decltype(ii_c)::value] = fragA(NxtSt{}, ii_c); });
         }
       }
-      if (u > 0) {
-        const int pj = (u - 1) / TM, pi = (u - 1) % TM;
-        const float s = (!T::STRADDLE || pj < j_switch) ? s_lo[pi] : s_hi[pi];
-        promote(acc[pi][pj], part[(u - 1) & 1], s);
+      part[(PH * STEPS + u) % P] = mfma_e4m3(fbr[(PH * TN + j) % R], fa[CA][i]);
+      if constexpr (i == 0) {
+        // column j+PD of this stage, or (past the end) column j+PD-TN of the next
+        constexpr int jn = j + PD;
+        constexpr int slot = (PH * TN + jn) % R;
+        if constexpr (jn < TN) fbr[slot] = fragB(CurSt{}, std::integral_constant<int, jn>{});
+        else fbr[slot] = fragB(NxtSt{}, std::integral_constant<int, jn - TN>{});
       }
+      if constexpr (!T::FA2 && j == TN - 1) fa[0][i] = fragA(NxtSt{}, std::integral_constant<int, i>{});
+      static_for<D>([&](auto d_c) {
+        constexpr int d = decltype(d_c)::value;
+        if constexpr (SPLIT) {
+          if constexpr (SCH::slot(d) == u) issue(d_c, CurSt{}, head);   // K-block kb+2
+        } else {
+          if constexpr (u >= PRE && SCH::slot(d) == u - PRE) issue(d_c, CurSt{}, head);
+          if constexpr (u < PRE && SCH::slot(d) == POST + u)
+            issue(d_c, std::integral_constant<int, TST>{}, tail);
+        }
+      });
+      promote_step(ph_c, u_c);
       step_fence();
-    }
-    {
-      const float s = (!T::STRADDLE || TN - 1 < j_switch) ? s_lo[TM - 1] : s_hi[TM - 1];
-      promote(acc[TM - 1][TN - 1], part[(STEPS - 1) & 1], s);
-    }
-    // the next stage's first columns sit in ring slots TN % 3 and (TN+1) % 3
-    if (TN % 3 != 0) {
-      const i32x8 c0 = fbr[TN % 3];
-      const i32x8 c1 = fbr[(TN + 1) % 3];
-      fbr[0] = c0;
-      fbr[1] = c1;
-    }
-    set_scales(sa_next, sb_next0, sb_next1);
-    stage = nstage;
+    });
+    set_scales(std::integral_constant<int, (PH + 1) & 1>{}, sa_next, sb_next0, sb_next1);
+    return ++kb == KB;
+  };
+  bool done = false;
+  for (;;) {
+    static_for<T::UNROLL>([&](auto ph_c) {
+      if (!done) done = kblock(ph_c);
+    });
+    if (done) break;
   }
+  // The last K-block's final PL partials, promoted once after the loop (an
+  // exit path per phase that did this work would keep the register allocator
+  // from holding each accumulator in one register across the phases).
+  {
+    const int last = (KB - 1) % T::UNROLL;
+    static_for<T::UNROLL>([&](auto ph_c) {
+      constexpr int PH = decltype(ph_c)::value;
+      if (last == PH) {
+        static_for<PL>([&](auto c_c) {
+          constexpr int w = STEPS - PL + decltype(c_c)::value;
+          promote(acc[w % TM][w / TM], part[(PH * STEPS + w) % P],
+                  scale_of(std::integral_constant<int, PH & 1>{}, std::integral_constant<int, w % TM>{},
+                           std::integral_constant<int, w / TM>{}));
+        });
+      }
+    });
+  }
+
 
   // ---- epilogue: bf16 RNE, staged through LDS so that every global store is
   // a full 16-byte piece of a contiguous output row
