@@ -49,7 +49,7 @@ using Cfg0 = fg::TileCfg<256, 256, 4, 2, 2, false, 2, false, 3>;   // large dens
 using Cfg1 = fg::TileCfg<256, 128, 4, 2, 3, false, 2, false, 3>;
 using Cfg2 = fg::TileCfg<128, 256, 2, 4, 3, false, 2, false, 3>;   // contiguous (BM | 128)
 using Cfg3 = fg::TileCfg<128, 128, 2, 2, 4, false, 3, false, 3>;
-using Cfg4 = fg::TileCfg<64, 112, 4, 1, 6, true, 6, true, 3>;     // skinny M, HBM-bound
+using Cfg4 = fg::TileCfg<64, 112, 4, 1, 6, true, 6, true, 3, 3>;     // skinny M, HBM-bound
 using Cfg5 = fg::TileCfg<256, 112, 4, 1, 3, true, 2, false, 3>;    // masked decode, HBM-bound
 constexpr Tile kTiles[] = {{256, 256, 1.00}, {256, 128, 0.95}, {128, 256, 0.95},
                            {128, 128, 0.80}, {64, 112, 0.50},  {256, 112, 0.90}};

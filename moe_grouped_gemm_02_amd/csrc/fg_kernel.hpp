@@ -85,7 +85,10 @@ constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 // Compile-time tile configuration.
 //   BM x BN   output tile per workgroup
 //   WGM x WGN waves per workgroup (each wave owns a (BM/WGM) x (BN/WGN) block)
-//   STAGES    depth of the LDS ring
+//   STAGES    depth of the LDS ring of B tiles
+//   ASTAGES   depth of the LDS ring of A tiles and scales (<= STAGES): the A
+//             operand is re-read from L2 by every N-tile and needs less
+//             buffering than B, which streams from HBM
 //   STRADDLE  a wave's columns may span two 128-wide scale blocks of B
 //   PD        B fragments are read PD sub-tile columns ahead of their MFMAs
 //             (a register ring of PD+1 fragments)
@@ -94,9 +97,10 @@ constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 //   PL        each MFMA's partial is promoted PL MFMAs after it was issued
 //             (a ring of PL+1 partials, slot = MFMA number modulo PL+1)
 template <int BM_, int BN_, int WGM_, int WGN_, int STAGES_, bool STRADDLE_, int PD_ = 2,
-          bool FA2_ = false, int PL_ = 1>
+          bool FA2_ = false, int PL_ = 1, int ASTAGES_ = STAGES_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, STAGES = STAGES_;
+  static constexpr int ASTAGES = ASTAGES_;
   static constexpr bool STRADDLE = STRADDLE_;
   static constexpr int PD = PD_, RING = PD_ + 1;
   static constexpr bool FA2 = FA2_;
@@ -117,24 +121,29 @@ struct TileCfg {
   static constexpr int A_BYTES = A_INSTR * W * 1024;
   static constexpr int B_BYTES = B_INSTR * W * 1024;
   static constexpr int SC_BYTES = BM * 4 + 256;
-  // LDS ring: the scale blocks of all stages, then the A tiles, then the B
+  // LDS rings: the scale blocks of all A stages, then the A tiles, then the B
   // tiles (scale reads then always fall within the first 64 KB)
   static constexpr int SC_BASE = 0;
-  static constexpr int A_BASE = STAGES * SC_BYTES;
-  static constexpr int B_BASE = A_BASE + STAGES * A_BYTES;
+  static constexpr int A_BASE = ASTAGES * SC_BYTES;
+  static constexpr int B_BASE = A_BASE + ASTAGES * A_BYTES;
   static constexpr int RING_BYTES = B_BASE + STAGES * B_BYTES;
   static constexpr int ROWB = BN * 2 + 16;   // staged bf16 output row (+16 B against bank conflicts)
   static constexpr int LDS_BYTES = RING_BYTES > BM * ROWB ? RING_BYTES : BM * ROWB;
+  // DMA instructions per wave per K-block, in the order A chunks, scale loads,
+  // B chunks
   static constexpr int DMA_PER_STAGE = A_INSTR + B_INSTR + SC_INSTR;
   // K-blocks per main-loop iteration: every per-K-block choice (ring stage,
   // B-ring slots, A-fragment set, scale set) repeats with this period, so each
   // copy of the K-block body works with compile-time registers and offsets
   static constexpr int UNROLL =
-      lcm_c(lcm_c(lcm_c(STAGES, RING / gcd_c(TN, RING)), PARTS / gcd_c(TM * TN, PARTS)), 2);
+      lcm_c(lcm_c(lcm_c(lcm_c(STAGES, ASTAGES), RING / gcd_c(TN, RING)), PARTS / gcd_c(TM * TN, PARTS)), 2);
   static_assert(WM % 16 == 0 && WN % 16 == 0 && TM >= 1 && TN >= 1, "wave tile must be 16-aligned");
   static_assert(BM % WGM == 0 && BN % WGN == 0, "waves must split the tile evenly");
   static_assert(BM % 64 == 0, "activation scales are loaded 64 rows at a time");
-  static_assert(STAGES >= 2, "need at least double buffering");
+  static_assert(ASTAGES >= 2 && ASTAGES <= STAGES, "need at least double buffering, A ring no deeper than B");
+  static_assert(STAGES != 2 || ASTAGES == 2, "the two-stage schedule uses one ring depth");
+  // a wave never has more loads in flight than the 6-bit vmcnt counter holds
+  static_assert(STAGES * DMA_PER_STAGE <= 63, "too many DMA instructions in flight per wave");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
   static_assert(WN <= 128, "a wave's columns may touch at most two scale blocks");
   static_assert(PD >= 1 && PD <= TN - 1, "prefetch distance must leave the barrier inside the K-block");
@@ -299,7 +308,7 @@ __device__ __forceinline__ void promote(f32x4& acc, const f32x4& part, float s) 
 template <int LAYOUT, class T>
 __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   constexpr int BM = T::BM, BN = T::BN, W = T::W, WM = T::WM, WN = T::WN;
-  constexpr int TM = T::TM, TN = T::TN, S = T::STAGES, PD = T::PD, R = T::RING;
+  constexpr int TM = T::TM, TN = T::TN, PD = T::PD, R = T::RING;
   constexpr int PL = T::PL, P = T::PARTS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
   __shared__ int s_group;
@@ -417,29 +426,32 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   }
   const uint32_t wave_at = lds_addr + wave * 1024;   // this wave's 1 KB DMA slot in a tile region
 
-  // scalar offsets of K-block kbd for the tile loads and for each scale load
+  // Scalar offsets of one DMA group: the A tile and scales of K-block ka and
+  // the B tile of K-block kbb (the two rings run different distances ahead).
   struct Soff {
-    uint32_t ab, sc[T::SC_INSTR];
+    uint32_t a, b, sc[T::SC_INSTR];
   };
-  auto soff_of = [&](int kbd) {
+  auto soff_of = [&](int ka, int kbb) {
     Soff o;
-    o.ab = (uint32_t)kbd * (uint32_t)kKBlock;
+    o.a = (uint32_t)ka * (uint32_t)kKBlock;
+    o.b = (uint32_t)kbb * (uint32_t)kKBlock;
 #pragma unroll
-    for (int q = 0; q < T::SC_INSTR; ++q) o.sc[q] = (uint32_t)kbd * sc_stride[q];
+    for (int q = 0; q < T::SC_INSTR; ++q) o.sc[q] = (uint32_t)ka * sc_stride[q];
     return o;
   };
-  constexpr int NA = T::A_INSTR, NB = T::B_INSTR;
-  // DMA instruction d (A chunks, then B chunks, then scale loads) of a K-block
-  // into ring stage ST
-  auto issue = [&](auto d_c, auto st_c, const Soff& o) {
-    constexpr int d = decltype(d_c)::value, ST = decltype(st_c)::value;
+  constexpr int NA = T::A_INSTR, NSC = T::SC_INSTR, NB = T::B_INSTR;
+  // DMA instruction d of a group (A chunks, then scale loads, then B chunks)
+  // into A-ring stage AST and B-ring stage BST
+  auto issue = [&](auto d_c, auto ast_c, auto bst_c, const Soff& o) {
+    constexpr int d = decltype(d_c)::value, AST = decltype(ast_c)::value, BST = decltype(bst_c)::value;
     if constexpr (d < NA) {
-      dma16<T::A_BASE + ST * T::A_BYTES + d * W * 1024>(rsA, a_off[d], o.ab, wave_at);
-    } else if constexpr (d < NA + NB) {
-      dma16<T::B_BASE + ST * T::B_BYTES + (d - NA) * W * 1024>(rsB, b_off[d - NA], o.ab, wave_at);
+      dma16<T::A_BASE + AST * T::A_BYTES + d * W * 1024>(rsA, a_off[d], o.a, wave_at);
+    } else if constexpr (d < NA + NSC) {
+      constexpr int q = d - NA;
+      dma4<AST * T::SC_BYTES>(rsS[q], sc_off[q], o.sc[q], sc_dst[q]);
     } else {
-      constexpr int q = d - NA - NB;
-      dma4<ST * T::SC_BYTES>(rsS[q], sc_off[q], o.sc[q], sc_dst[q]);
+      constexpr int q = d - NA - NSC;
+      dma16<T::B_BASE + BST * T::B_BYTES + q * W * 1024>(rsB, b_off[q], o.b, wave_at);
     }
   };
 
@@ -475,13 +487,18 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
     return frag_at<T::B_BASE + decltype(st_c)::value * T::B_BYTES + decltype(j_c)::value * 2048>(bLo, bHi);
   };
 
-  // ---- DMA schedule. K-block x lands in ring stage x % S.
+  // ---- DMA schedule. The A tile and scales of K-block x land in A-ring
+  // stage x % SA, its B tile in B-ring stage x % SB.
   //
-  // S >= 3: x's stage is freed at the barrier of K-block x-S and must be
-  // complete at the barrier of K-block x-1. Its instructions are spread one per
-  // pipeline step over the K-block after the freeing barrier ("head" after that
-  // barrier, "tail" before the next one), leaving a further full K-block for
-  // the loads to land.
+  // SB >= 3: DMA group g(kb) holds the A tile and scales of K-block kb+SA and
+  // the B tile of K-block kb+SB, whose stages the barrier of K-block kb has
+  // just freed. Its instructions are spread one per pipeline step over the
+  // K-block after that barrier ("head" after it, "tail" before the next one).
+  // Groups are issued in order and loads complete in issue order, so at the
+  // barrier of K-block kb, which needs K-block kb+1, everything issued after
+  // the A part of group g(kb+1-SA) may still be in flight: its B part (the B
+  // tile of an older K-block is already complete when SB > SA) and the
+  // groups g(kb+2-SA) .. g(kb-1).
   //
   // S == 2: each K-block takes two barriers. The A fragments are held in
   // registers for the whole K-block, so a stage's A half is free once column 0
@@ -498,26 +515,35 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   constexpr int STEPS = SCH::STEPS, PRE = SCH::PRE, POST = SCH::POST, D = SCH::D;
   constexpr bool SPLIT = SCH::SPLIT;
   constexpr int N_HEAD = SCH::n_head(), N_EARLY = SCH::n_early();
-  static_assert((S - 2) * D + N_HEAD < 64 && D + N_EARLY < 64, "vmcnt counter range");
+  constexpr int SA = T::ASTAGES, SB = T::STAGES;
+  constexpr int B_AFTER_A = SA == SB ? 0 : NB;   // a group's loads that may trail its A part
+  constexpr int WAIT_LOOP = SPLIT ? N_EARLY : B_AFTER_A + (SA - 2) * D;
+  constexpr int WAIT_PRO = SPLIT ? D : B_AFTER_A + (SA - 2) * D + N_HEAD;
+  static_assert(WAIT_PRO < 64 && WAIT_LOOP < 64, "vmcnt counter range");
 
-  // ---- prologue: wait for K-block 0 with the later ones in flight
-  //   S >= 3: K-blocks 1 .. S-2 and the head of K-block S-1
-  //   S == 2: K-block 1
-  static_for<S - 1>([&](auto x_c) {
-    const Soff o = soff_of(min((int)decltype(x_c)::value, KB - 1));
-    static_for<D>([&](auto d_c) { issue(d_c, x_c, o); });
-  });
+  // ---- prologue: the groups g(-SB) .. g(-1) (the last one only its head),
+  // i.e. the B tiles of K-blocks 0 .. SB-1 and the A tiles of 0 .. SA-1, then
+  // wait for K-block 0
   if constexpr (SPLIT) {
-    const Soff o = soff_of(min(1, KB - 1));
-    static_for<D>([&](auto d_c) { issue(d_c, std::integral_constant<int, 1>{}, o); });
-    wait_vm<D>();
-  } else {
-    const Soff o = soff_of(min(S - 1, KB - 1));
-    static_for<D>([&](auto d_c) {
-      if constexpr (SCH::slot(decltype(d_c)::value) < POST) issue(d_c, std::integral_constant<int, S - 1>{}, o);
+    static_for<2>([&](auto x_c) {
+      constexpr int x = decltype(x_c)::value;
+      const Soff o = soff_of(min(x, KB - 1), min(x, KB - 1));
+      static_for<D>([&](auto d_c) { issue(d_c, x_c, x_c, o); });
     });
-    wait_vm<(S - 2) * D + N_HEAD>();
+  } else {
+    static_for<SB>([&](auto x_c) {
+      constexpr int x = decltype(x_c)::value;       // group g(x - SB)
+      constexpr int ka = x - SB + SA;               // its A K-block (< 0: none)
+      const Soff o = soff_of(min(ka < 0 ? 0 : ka, KB - 1), min(x, KB - 1));
+      static_for<D>([&](auto d_c) {
+        constexpr int d = decltype(d_c)::value;
+        constexpr bool a_part = d < NA + NSC;
+        if constexpr (!(a_part && ka < 0) && !(x == SB - 1 && SCH::slot(d) >= POST))
+          issue(d_c, std::integral_constant<int, (ka < 0 ? 0 : ka)>{}, x_c, o);
+      });
+    });
   }
+  wait_vm<WAIT_PRO>();
   block_barrier();
 
   // Register state. B fragments live in a ring of R = PD+1 (column g of the
@@ -615,12 +641,16 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   int kb = 0;
   auto kblock = [&](auto ph_c) -> bool {
     constexpr int PH = decltype(ph_c)::value;
-    constexpr int ST = PH % S, NST = (PH + 1) % S, TST = (PH + S - 1) % S;
-    constexpr int CA = T::FA2 ? (PH & 1) : 0, NA_SET = T::FA2 ? ((PH + 1) & 1) : 0;
-    using CurSt = std::integral_constant<int, ST>;
-    using NxtSt = std::integral_constant<int, NST>;
-    const Soff head = soff_of(min(kb + S, KB - 1));        // K-block kb+S into stage ST
-    const Soff tail = soff_of(min(kb + S - 1, KB - 1));    // K-block kb+S-1 into stage TST (S >= 3)
+    constexpr int U = T::UNROLL;
+    constexpr int CA = PH % SA, NXA = (PH + 1) % SA, TA = (PH + U - 1) % SA;   // A ring: this, next, tail group
+    constexpr int CB = PH % SB, NXB = (PH + 1) % SB, TB = (PH + U - 1) % SB;   // B ring
+    constexpr int FSET = T::FA2 ? (PH & 1) : 0, NFSET = T::FA2 ? ((PH + 1) & 1) : 0;
+    using CurA = std::integral_constant<int, CA>;
+    using NxtA = std::integral_constant<int, NXA>;
+    using CurB = std::integral_constant<int, CB>;
+    using NxtB = std::integral_constant<int, NXB>;
+    const Soff head = soff_of(min(kb + SA, KB - 1), min(kb + SB, KB - 1));           // group g(kb)
+    const Soff tail = soff_of(min(kb - 1 + SA, KB - 1), min(kb - 1 + SB, KB - 1));   // group g(kb-1)
     (void)tail;
     float sa_next[TM], sb_next0 = 0.f, sb_next1 = 0.f;
     static_for<STEPS>([&](auto u_c) {
@@ -631,30 +661,30 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
         // every read of the current stage has been issued; the next stage (and,
         // for S == 2, every DMA older than this K-block's early A loads) is in
         wait_lgkm0();
-        wait_vm<(S - 2) * D + N_EARLY>();
+        wait_vm<WAIT_LOOP>();
         block_barrier();
-        scale_read(NxtSt{}, sa_next, sb_next0, sb_next1);
+        scale_read(NxtA{}, sa_next, sb_next0, sb_next1);
         if constexpr (T::FA2) {
-          static_for<TM>([&](auto ii_c) { fa[NA_SET][decltype(ii_c)::value] = fragA(NxtSt{}, ii_c); });
+          static_for<TM>([&](auto ii_c) { fa[NFSET][decltype(ii_c)::value] = fragA(NxtA{}, ii_c); });
         }
       }
-      part[(PH * STEPS + u) % P] = mfma_e4m3(fbr[(PH * TN + j) % R], fa[CA][i]);
+      part[(PH * STEPS + u) % P] = mfma_e4m3(fbr[(PH * TN + j) % R], fa[FSET][i]);
       if constexpr (i == 0) {
         // column j+PD of this stage, or (past the end) column j+PD-TN of the next
         constexpr int jn = j + PD;
         constexpr int slot = (PH * TN + jn) % R;
-        if constexpr (jn < TN) fbr[slot] = fragB(CurSt{}, std::integral_constant<int, jn>{});
-        else fbr[slot] = fragB(NxtSt{}, std::integral_constant<int, jn - TN>{});
+        if constexpr (jn < TN) fbr[slot] = fragB(CurB{}, std::integral_constant<int, jn>{});
+        else fbr[slot] = fragB(NxtB{}, std::integral_constant<int, jn - TN>{});
       }
-      if constexpr (!T::FA2 && j == TN - 1) fa[0][i] = fragA(NxtSt{}, std::integral_constant<int, i>{});
+      if constexpr (!T::FA2 && j == TN - 1) fa[0][i] = fragA(NxtA{}, std::integral_constant<int, i>{});
       static_for<D>([&](auto d_c) {
         constexpr int d = decltype(d_c)::value;
         if constexpr (SPLIT) {
-          if constexpr (SCH::slot(d) == u) issue(d_c, CurSt{}, head);   // K-block kb+2
+          if constexpr (SCH::slot(d) == u) issue(d_c, CurA{}, CurB{}, head);   // K-block kb+2
         } else {
-          if constexpr (u >= PRE && SCH::slot(d) == u - PRE) issue(d_c, CurSt{}, head);
+          if constexpr (u >= PRE && SCH::slot(d) == u - PRE) issue(d_c, CurA{}, CurB{}, head);
           if constexpr (u < PRE && SCH::slot(d) == POST + u)
-            issue(d_c, std::integral_constant<int, TST>{}, tail);
+            issue(d_c, std::integral_constant<int, TA>{}, std::integral_constant<int, TB>{}, tail);
         }
       });
       promote_step(ph_c, u_c);
