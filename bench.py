@@ -235,11 +235,17 @@ def cpu_baseline(name, target_s):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and whitespace removed, so that
+    editing a comment does not detach the committed counters from the code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,26 +10,27 @@
 // sub-tile with a zero C operand (a fresh FP32 partial covering exactly one
 // scale block), followed by one v_fma_f32 per output element that adds
 // partial * (sa * sb) into the master accumulator held in VGPRs. Each MFMA's
-// promotion is issued after the next MFMA, so the VALU work overlaps the
-// matrix core instead of waiting on it.
+// promotion is issued a few MFMAs after it, so the VALU work overlaps the
+// matrix core instead of waiting on its result.
 //
 // Data movement (the pages' "data movement / compute / epilogue" overlap,
 // "Technical details > thread specialisation", done the gfx950 way): every
-// wave issues direct global->LDS loads (global_load_lds_dwordx4, no VGPR
-// staging) for its share of the next K-blocks into an S-stage ring of LDS
-// buffers, so there are no producer waves; one workgroup barrier per K-block
-// both publishes the next stage and frees the stage just consumed. The
-// barrier sits before the last column of MFMAs, so the next K-block's
-// fragments are read from LDS while those MFMAs run.
+// wave issues direct global->LDS loads (buffer_load ... lds, no VGPR staging)
+// for its share of later K-blocks, so there are no producer waves. A tiles
+// and scales go into one ring of LDS stages, B tiles into a second ring that
+// may run further ahead (B streams from HBM; A is re-read from L2 by every
+// N-tile). One workgroup barrier per K-block both publishes the next stage
+// and frees the stages just consumed. The barrier sits before the last
+// columns of MFMAs, so the next K-block's fragments are read from LDS while
+// those MFMAs run.
 //
-// LDS layout of a stage: A tile [BM rows][128 B], B tile [BN rows][128 B],
-// then BM activation scales and the weight scales of the tile's 128-column
-// blocks (fp32), so every operand of a K-block arrives through the same
-// counted DMA stream. A 16-byte chunk c of tile row r is stored
-// at chunk position c ^ (r & 7) (XOR swizzle): the 16 rows a quarter-wave
-// reads for one chunk index hit distinct bank groups. The swizzle is applied
-// by choosing which global chunk each DMA lane fetches, since a DMA lane's LDS
-// destination is fixed (lane * 16 bytes after the wave's base).
+// LDS layout: the scale blocks of all A stages (BM activation scales and the
+// weight scales of the tile's 128-column blocks, fp32), then the A tiles
+// [BM rows][128 B], then the B tiles [BN rows][128 B]. A 16-byte chunk c of
+// tile row r is stored at chunk position c ^ (r & 7) (XOR swizzle): the 16
+// rows a quarter-wave reads for one chunk index hit distinct bank groups. The
+// swizzle is applied by choosing which global chunk each DMA lane fetches,
+// since a DMA lane's LDS destination is fixed (lane * 16 bytes after M0).
 //
 // Operand roles. The MFMA's first operand is fed with rows of B (output
 // columns n), its second with rows of A (output rows m). The 16x16 result then
