@@ -235,8 +235,10 @@ def cpu_baseline(name, target_s):
 
 
 def kernel_source_hash():
-    """Hash of the kernel sources with comments and whitespace removed, so that
-    editing a comment does not detach the committed counters from the code."""
+    """Hash of what defines the kernels: the kernel template with comments and
+    whitespace removed, and the tile-configuration lines that instantiate it.
+    Editing a comment or the host-side tile choice does not detach the
+    committed counters from the code they were taken on."""
     import hashlib
     import re
     h = hashlib.sha256()
@@ -245,6 +247,8 @@ def kernel_source_hash():
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
+        if f.endswith(".hip"):
+            text = "\n".join(re.findall(r"using Cfg\d+ = fg::TileCfg<[^>]*>;", text))
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 

@@ -40,8 +40,8 @@ int current_device(int* cus) {
 
 // ---------------------------------------------------------------- tiles
 struct Tile {
-  int bm, bn;
-  double eff;   // relative MFMA efficiency of one tile (larger tiles reuse more)
+  int bm, bn, waves;
+  double eff;   // fraction of the matrix-core rate the tile's K loop sustains
 };
 // Compiled tile shapes (rows x cols of D per workgroup), in the order of the
 // launch switch below.
@@ -51,8 +51,9 @@ using Cfg2 = fg::TileCfg<128, 256, 2, 4, 3, false, 2, false, 3>;   // contiguous
 using Cfg3 = fg::TileCfg<128, 128, 2, 2, 4, false, 3, false, 3>;
 using Cfg4 = fg::TileCfg<64, 112, 4, 1, 6, true, 6, true, 3, 3>;     // skinny M, HBM-bound
 using Cfg5 = fg::TileCfg<256, 112, 4, 1, 3, true, 2, false, 3>;    // masked decode, HBM-bound
-constexpr Tile kTiles[] = {{256, 256, 1.00}, {256, 128, 0.95}, {128, 256, 0.95},
-                           {128, 128, 0.80}, {64, 112, 0.50},  {256, 112, 0.90}};
+constexpr Tile kTiles[] = {{256, 256, Cfg0::W, 0.70}, {256, 128, Cfg1::W, 0.75},
+                           {128, 256, Cfg2::W, 0.75}, {128, 128, Cfg3::W, 0.70},
+                           {64, 112, Cfg4::W, 0.60},  {256, 112, Cfg5::W, 0.70}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kDefaultCUs = 256;
 
@@ -68,22 +69,31 @@ long count_tiles(int layout, int M, int N, int G, const Tile& t) {
 }
 
 // Picks the tile for a problem: the compiled shape with the smallest
-// estimated time, (waves of tiles over the CUs) x (tile area / tile
-// efficiency). The wave count carries the quantisation loss the zwzgs.cn
-// DeepGEMM page describes ("non-standard block sizes": a tile count just
-// above a multiple of the SM count leaves most of the last wave idle); the
-// area term carries the padding waste of partial tiles. Contiguous tiles must
-// not straddle an aligned 128-row expert block.
-int pick_tile(int layout, int M, int N, int G, int cus) {
+// estimated time, in CU cycles. One K-block of a tile costs the larger of its
+// matrix-core time (BM*BN*256 FLOP at 8192 FLOP/clk per CU, derated by the
+// tile's sustained fraction) and its global->LDS time ((BM+BN)*128 bytes at
+// the per-CU rate the GEMM sustains: ~24 B/clk with 4 issuing waves, ~30 with
+// 8); each tile adds a fixed prologue/epilogue cost. Tiles run in rounds over
+// the CUs, which carries the wave-quantisation loss the zwzgs.cn DeepGEMM
+// page describes ("non-standard block sizes": a tile count just above a
+// multiple of the SM count leaves most of the last round idle); partial tiles
+// carry their padding. Contiguous tiles must not straddle an aligned 128-row
+// expert block.
+constexpr double kTileFixedCycles = 4000.0;
+int pick_tile(int layout, int M, int N, int K, int G, int cus) {
   const int forced = g_forced_tile.load(std::memory_order_relaxed);
   if (forced >= 0) return forced;
   int best = -1;
   double best_cost = 0.0;
+  const double kblocks = K / 128;
   for (int i = 0; i < kNumTiles; ++i) {
-    if (layout == FG_LAYOUT_CONTIGUOUS && 128 % kTiles[i].bm != 0) continue;
-    const long tiles = count_tiles(layout, M, N, G, kTiles[i]);
-    const long waves = (tiles + cus - 1) / cus;
-    const double cost = (double)waves * kTiles[i].bm * kTiles[i].bn / kTiles[i].eff;
+    const Tile& t = kTiles[i];
+    if (layout == FG_LAYOUT_CONTIGUOUS && 128 % t.bm != 0) continue;
+    const long tiles = count_tiles(layout, M, N, G, t);
+    const long rounds = (tiles + cus - 1) / cus;
+    const double t_mfma = (double)t.bm * t.bn * 256.0 / (8192.0 * t.eff);
+    const double t_mem = (double)(t.bm + t.bn) * 128.0 / (t.waves >= 8 ? 30.0 : 24.0);
+    const double cost = (double)rounds * (kblocks * (t_mfma > t_mem ? t_mfma : t_mem) + kTileFixedCycles);
     if (best < 0 || cost < best_cost * (1.0 - 1e-9)) {
       best = i;
       best_cost = cost;
@@ -128,7 +138,7 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   const int st = current_device(&cus);
   if (st != FG_OK) return st;
 
-  const int ti = pick_tile(layout, M, N, G, cus);
+  const int ti = pick_tile(layout, M, N, K, G, cus);
   const Tile& t = kTiles[ti];
   // contiguous tiles must not straddle an aligned 128-row expert block
   if (layout == FG_LAYOUT_CONTIGUOUS && 128 % t.bm != 0) return FG_EINVAL;
@@ -188,7 +198,7 @@ int fg_select_config(int layout, int M, int N, int K, int G, int num_cus, int* b
   if (M < 0 || N < 0 || K < 0 || (layout != FG_LAYOUT_DENSE && G < 1)) return FG_EINVAL;
   if (layout == FG_LAYOUT_DENSE) G = 1;
   const int cus = num_cus > 0 ? num_cus : kDefaultCUs;
-  const int ti = pick_tile(layout, M, N, G, cus);
+  const int ti = pick_tile(layout, M, N, K, G, cus);
   if (bm) *bm = kTiles[ti].bm;
   if (bn) *bn = kTiles[ti].bn;
   if (grid) *grid = (int)count_tiles(layout, M, N, G, kTiles[ti]);

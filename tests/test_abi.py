@@ -98,6 +98,18 @@ def test_select_config_fills_the_machine():
             assert 128 % bm == 0         # contiguous tiles never straddle an expert block
 
 
+def test_select_config_picks_the_measured_best_tiles():
+    # The cost model's choices for the five workloads are the tiles that timed
+    # fastest on an MI355X when every compiled tile was forced in turn: the
+    # smallest tile that gives 256 workgroups for M=256, the largest tiles for
+    # the big dense and masked problems (fewer re-reads of A and B), and the
+    # widest tile with BM | 128 for the contiguous layout.
+    assert fg.select_config(0, 256, 7168, 7168, 1)[:2] == (64, 112)
+    assert fg.select_config(1, 9472, 4096, 7168, 8)[:2] == (128, 256)
+    assert fg.select_config(2, 256, 7168, 2048, 16)[:2] == (256, 256)
+    assert fg.select_config(0, 8192, 7168, 18432, 1)[:2] in ((256, 128), (256, 256))
+
+
 def test_select_config_rejects_bad_layout():
     with pytest.raises(fg.FGError):
         fg.select_config(7, 128, 128, 128)
