@@ -192,3 +192,30 @@ def test_every_tile_contiguous(forced_tile):
     ref, valid = oracle.ref_contiguous(A, sa, B, sb, mi)
     r = oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
     assert r["ok"], r
+
+
+@pytest.mark.parametrize("forced_tile", TILES, indirect=True, ids=lambda t: f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("K", [128, 256])
+def test_every_tile_fewer_kblocks_than_stages(forced_tile, K):
+    """One and two K-blocks: every LDS ring is deeper than the problem, so all
+    later loads are the clamped repeats of the last K-block."""
+    print(f"tile {forced_tile} dense K={K}", flush=True)
+    A, sa, B, sb = make_dense(100, 256, K, 70 + K)
+    out = run_dense(A, sa, B, sb)
+    r = oracle.check(out, oracle.ref_dense(A, sa, B, sb))
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("forced_tile,kblocks",
+                         [((64, 112), kb) for kb in range(1, 14)] + [((256, 256), kb) for kb in range(1, 8)],
+                         indirect=["forced_tile"], ids=lambda v: f"{v[0]}x{v[1]}" if isinstance(v, tuple) else f"kb{v}")
+def test_every_loop_exit_phase(forced_tile, kblocks):
+    """The K loop is unrolled over 12 (64x112) or 6 (256x256) K-blocks and
+    finishes the last partials in a branch per exit phase; these K lengths
+    end the loop in every phase."""
+    K = 128 * kblocks
+    print(f"tile {forced_tile} dense K={K}", flush=True)
+    A, sa, B, sb = make_dense(80, 384, K, 90 + kblocks)
+    out = run_dense(A, sa, B, sb)
+    r = oracle.check(out, oracle.ref_dense(A, sa, B, sb))
+    assert r["ok"], r
