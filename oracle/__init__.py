@@ -9,7 +9,8 @@ What it computes (fp64 throughout, numpy):
   * ``e4m3``  -- the 256-entry OCP E4M3 decode table and a round-to-nearest-even
                  encoder with saturation at 448.
   * ``quant`` -- per 1x128 (activation) and per 128x128 (weight) block
-                 quantisation with scale = amax / 448.
+                 quantisation with scale = amax / 448, or that scale rounded
+                 up to a power of two (the E8M0 / micro-scaling variant).
   * ``gemm``  -- D = A . B^T as "dequantise, then one fp64 GEMM" for the dense,
                  grouped-contiguous and grouped-masked layouts, plus the
                  two-level (per 128-wide K-block partial, then scale and add)
@@ -31,7 +32,8 @@ rational arithmetic, integer matmul, closed forms, invariants).
 """
 
 from .e4m3 import decode_table, encode_rne, E4M3_MAX  # noqa: F401
-from .quant import quantize_blocks, quantize_act_1x128, quantize_weight_128x128  # noqa: F401
+from .quant import (quantize_blocks, quantize_act_1x128, quantize_weight_128x128,  # noqa: F401
+                    pow2_ceil_scale)
 from .gemm import (  # noqa: F401
     dequant_act,
     dequant_weight,

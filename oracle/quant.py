@@ -16,6 +16,14 @@ out-of-range values are clipped/saturated. Readings taken where the pages stop:
     land one ulp beyond 448), then rounded to nearest E4M3, ties to even.
 
 The dequantised value of a code is decode(code) * scale.
+
+Power-of-two scales (``pow2=True``). The 2kiu.com explainer, section 7 (where
+it points beyond FP8), names MX / micro-scaling formats, whose block scales are
+pure powers of two (an 8-bit exponent, E8M0). Reading taken for that variant:
+the scale is the fp32 scale above rounded UP to the next power of two (so
+x / scale still lies within [-448, 448] and the division is exact), and never
+below 2^-126, the smallest normal fp32 value (every such scale is then an
+E8M0 code 2^(e - 127) with e in 1..254).
 """
 
 import numpy as np
@@ -23,10 +31,25 @@ import numpy as np
 from .e4m3 import E4M3_MAX, encode_rne
 
 
-def quantize_blocks(x, block_rows, block_cols):
+def pow2_ceil_scale(scale):
+    """Smallest power of two >= each fp32 scale, floored at 2^-126 (fp32 out).
+
+    frexp writes a positive s as m * 2^e with m in [0.5, 1): s is itself a power
+    of two exactly when m == 0.5, otherwise the next power of two up is 2^e.
+    """
+    s = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    if np.any(~(s > 0)) or np.any(~np.isfinite(s)):
+        raise ValueError("pow2_ceil_scale: scales must be positive and finite")
+    m, e = np.frexp(s)
+    p = np.where(m == 0.5, s, np.ldexp(1.0, e))
+    return np.maximum(p, 2.0 ** -126).astype(np.float32)
+
+
+def quantize_blocks(x, block_rows, block_cols, pow2=False):
     """Quantise a 2-D fp32 array in (block_rows x block_cols) blocks.
 
     Returns (codes uint8 same shape as x, scales fp32 [R/block_rows, C/block_cols]).
+    With pow2=True every scale is rounded up to a power of two first.
     """
     x = np.asarray(x, dtype=np.float32)
     R, C = x.shape
@@ -37,25 +60,27 @@ def quantize_blocks(x, block_rows, block_cols):
     amax = np.abs(blocks).max(axis=(1, 3))                      # fp32, exact
     scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)    # fp32 division
     scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
+    if pow2:
+        scale = pow2_ceil_scale(scale)
     y = (blocks / scale[:, None, :, None]).astype(np.float32)   # fp32 division
     y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     codes = encode_rne(y).reshape(R, C)
     return codes, scale
 
 
-def quantize_act_1x128(x):
+def quantize_act_1x128(x, pow2=False):
     """Activation quantisation: x fp32 [M, K] -> codes [M, K], sa fp32 [M, K/128]."""
-    return quantize_blocks(x, 1, 128)
+    return quantize_blocks(x, 1, 128, pow2)
 
 
-def quantize_weight_128x128(w):
+def quantize_weight_128x128(w, pow2=False):
     """Weight quantisation: w fp32 [N, K] (or [G, N, K]) -> codes, sb [N/128, K/128]
     (or [G, N/128, K/128])."""
     w = np.asarray(w, dtype=np.float32)
     if w.ndim == 2:
-        return quantize_blocks(w, 128, 128)
+        return quantize_blocks(w, 128, 128, pow2)
     codes = np.empty(w.shape, dtype=np.uint8)
     scales = np.empty((w.shape[0], w.shape[1] // 128, w.shape[2] // 128), dtype=np.float32)
     for g in range(w.shape[0]):
-        codes[g], scales[g] = quantize_blocks(w[g], 128, 128)
+        codes[g], scales[g] = quantize_blocks(w[g], 128, 128, pow2)
     return codes, scales
