@@ -20,7 +20,9 @@ the GEMM kernel, from HIP events recorded on the launch stream around the timed
 steps. `cpu_baseline` is the CPU oracle (dequantise + fp64 GEMM) timed on this
 host. `per_workload` repeats the measurement for the other workloads (the small
 dense case, MoE contiguous, MoE masked, the large dense FFN GEMM) unless
---headline-only is given.
+--headline-only is given; `per_workload_pow2` measures every workload again on
+the power-of-two-scale entry points (E8M0 scales applied by the matrix core),
+with operands quantised by the power-of-two quantisers.
 """
 import argparse
 import ctypes
@@ -53,6 +55,11 @@ def parse():
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline workload (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--scales", choices=("fp32", "pow2"), default="fp32",
+                    help="block scales of the headline run: fp32 (amax/448) or powers of two "
+                         "on the _pow2 entry points")
+    ap.add_argument("--no-pow2", action="store_true",
+                    help="skip the per-workload measurements of the power-of-two path")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle baseline sample")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
@@ -66,9 +73,10 @@ def parse():
 
 
 # --------------------------------------------------------------------- inputs
-def gpu_operands(name, fg, torch):
+def gpu_operands(name, fg, torch, pow2=False):
     """Seeded fp32 inputs (numpy) -> device -> E4M3 + scales by the library's
-    quantisers. Returns a dict of device tensors and the sizes."""
+    quantisers (pow2: the power-of-two-scale quantisers). Returns a dict of
+    device tensors and the sizes."""
     import numpy as np
     import workloads
 
@@ -76,10 +84,14 @@ def gpu_operands(name, fg, torch):
     dev = torch.device("cuda", 0)
     a = torch.from_numpy(w["a"]).to(dev)
     b = torch.from_numpy(w["b"]).to(dev)
-    A, sa = fg.quant_act_1x128(a)
-    B, sb = fg.quant_weight_128x128(b)
+    if pow2:
+        A, sa = fg.quant_act_1x128_pow2(a)
+        B, sb = fg.quant_weight_128x128_pow2(b)
+    else:
+        A, sa = fg.quant_act_1x128(a)
+        B, sb = fg.quant_weight_128x128(b)
     del a, b
-    op = dict(kind=w["kind"], A=A, sa=sa, B=B, sb=sb)
+    op = dict(kind=w["kind"], A=A, sa=sa, B=B, sb=sb, pow2=pow2)
     N, K = w["b"].shape[-2], w["b"].shape[-1]
     op.update(N=N, K=K, flop=workloads.useful_flop(w))
     if w["kind"] == "dense":
@@ -140,19 +152,20 @@ def make_step(op, copies, fg, torch):
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     D = P(op["D"])
     M, N, K, G = op["M"], op["N"], op["K"], op["G"]
+    sfx = "_pow2" if op["pow2"] else ""
     calls = []
     for c in copies:
         if op["kind"] == "dense":
             args = (P(c["A"]), P(c["sa"]), P(c["B"]), P(c["sb"]), D, M, N, K, stream)
-            calls.append((L.fg_gemm_fp8_nt, args))
+            calls.append((getattr(L, "fg_gemm_fp8_nt" + sfx), args))
         elif op["kind"] == "contiguous":
             args = (P(c["A"]), P(c["sa"]), P(c["B"]), P(c["sb"]), D, P(op["m_indices"]),
                     M, N, K, G, stream)
-            calls.append((L.fg_grouped_contiguous, args))
+            calls.append((getattr(L, "fg_grouped_contiguous" + sfx), args))
         else:
             args = (P(c["A"]), P(c["sa"]), P(c["B"]), P(c["sb"]), D, P(op["masked_m"]),
                     G, M, N, K, stream)
-            calls.append((L.fg_grouped_masked, args))
+            calls.append((getattr(L, "fg_grouped_masked" + sfx), args))
 
     def step(i):
         f, a = calls[i % len(calls)]
@@ -162,8 +175,8 @@ def make_step(op, copies, fg, torch):
     return step
 
 
-def time_workload(name, steps, warmup, fg, torch):
-    op = gpu_operands(name, fg, torch)
+def time_workload(name, steps, warmup, fg, torch, pow2=False):
+    op = gpu_operands(name, fg, torch, pow2)
     copies = replicate(op, torch)
     step = make_step(op, copies, fg, torch)
     for i in range(warmup):
@@ -371,7 +384,8 @@ def main():
         print("bench.py: no HIP device", file=sys.stderr)
         sys.exit(1)
     fg.lib()
-    head = time_workload(args.workload, args.steps, args.warmup, fg, torch)
+    head_pow2 = args.scales == "pow2"
+    head = time_workload(args.workload, args.steps, args.warmup, fg, torch, head_pow2)
     hs = summarize(head)
     op = head["op"]
     value = op["flop"] / (head["wall_ms"] * 1e-3) / 1e12
@@ -398,14 +412,24 @@ def main():
         for name in ORDER:
             if name == args.workload:
                 continue
-            r = time_workload(name, max(5, args.steps // 2), max(2, args.warmup // 2), fg, torch)
+            r = time_workload(name, max(5, args.steps // 2), max(2, args.warmup // 2), fg, torch,
+                              head_pow2)
             per[name] = summarize(r)
+            del r
+            torch.cuda.empty_cache()
+    per_pow2 = None
+    if not args.headline_only and not args.no_pow2:
+        per_pow2 = {}
+        for name in ORDER:
+            r = time_workload(name, max(5, args.steps // 2), max(2, args.warmup // 2), fg, torch,
+                              not head_pow2)
+            per_pow2[name] = summarize(r)
             del r
             torch.cuda.empty_cache()
 
     if args.calibrate_copy_mb:
         copy_calibration(args.calibrate_copy_mb, torch)
-    roof["traffic"] = measured_traffic(args.workload)
+    roof["traffic"] = measured_traffic(args.workload) if not head_pow2 else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -425,12 +449,15 @@ def main():
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": args.workload, "layout": op["kind"], "M": op["M"], "N": op["N"],
-                   "K": op["K"], "G": op["G"], "scales": "1x128 (A), 128x128 (B), fp32",
+                   "K": op["K"], "G": op["G"],
+                   "scales": "1x128 (A), 128x128 (B), " + ("powers of two (E8M0 on the matrix core)"
+                                                          if head_pow2 else "fp32"),
                    "out": "bf16", "tile": hs["tile"], "input_copies": hs["input_copies"],
                    "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_workload": per,
+        ("per_workload_fp32" if head_pow2 else "per_workload_pow2"): per_pow2,
     }
     print(json.dumps(line), flush=True)
 

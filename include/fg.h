@@ -101,6 +101,32 @@ int fg_grouped_masked(const void* A, const float* sa, const void* B, const float
                       hipStream_t stream);
 
 /*
+ * Power-of-two block scales on the matrix core (E8M0). The 2kiu.com DeepGEMM
+ * explainer, section 7, names MX / micro-scaling formats as the next step
+ * beyond per-block FP8 scaling; their block scales are pure powers of two.
+ * These three calls compute the same D as fg_gemm_fp8_nt /
+ * fg_grouped_contiguous / fg_grouped_masked -- same arguments, layouts,
+ * ownership, row rules and error codes -- under one more precondition: every
+ * sa and sb entry must be a power of two between 2^-126 and 2^127 (a normal
+ * fp32 value with a zero mantissa; fg_quant_*_pow2 produce such scales). Its
+ * exponent field is then the E8M0 code (2^(e-127)) that gfx950's
+ * v_mfma_scale_f32_16x16x128_f8f6f4 applies per row and K-block inside the
+ * matrix core, accumulating every K-block straight into the FP32 master
+ * accumulator; no promotion step runs on the vector ALUs. Accumulation is
+ * FP32 throughout, as in the two-level form. A scale that is not such a power
+ * of two is not detected: its mantissa is ignored (the result is then that of
+ * the scale rounded down to a power of two); memory safety is unaffected.
+ */
+int fg_gemm_fp8_nt_pow2(const void* A, const float* sa, const void* B, const float* sb,
+                        void* D, int M, int N, int K, hipStream_t stream);
+int fg_grouped_contiguous_pow2(const void* A, const float* sa, const void* B, const float* sb,
+                               void* D, const int32_t* m_indices, int M, int N, int K, int G,
+                               hipStream_t stream);
+int fg_grouped_masked_pow2(const void* A, const float* sa, const void* B, const float* sb,
+                           void* D, const int32_t* masked_m, int G, int M_max, int N, int K,
+                           hipStream_t stream);
+
+/*
  * Tile configuration the library would launch for a problem, computed on the
  * host from sizes only (no device access, usable without a GPU). Tiles are
  * chosen from a fixed table to minimise wave quantisation over `num_cus`
@@ -141,6 +167,17 @@ int fg_quant_act_1x128(const float* x, void* q, float* sa, int batch, int M, int
  *   fp32 (= [G][N/128][K/128]). */
 int fg_quant_weight_128x128(const float* w, void* q, float* sb, int rows, int K,
                             hipStream_t stream);
+
+/* Power-of-two variants of the two quantisers (same arguments, layouts and
+ * errors): each block's scale amax / 448 (1 for an all-zero block) is rounded
+ * up to the next power of two and floored at 2^-126, so x / scale is exact and
+ * lies within [-448, 448]. Their scales satisfy the precondition of the
+ * fg_*_pow2 GEMM calls. Reading taken for the MX scale rule, which the pages
+ * name (2kiu.com explainer, section 7) without defining. */
+int fg_quant_act_1x128_pow2(const float* x, void* q, float* sa, int batch, int M, int K,
+                            hipStream_t stream);
+int fg_quant_weight_128x128_pow2(const float* w, void* q, float* sb, int rows, int K,
+                                 hipStream_t stream);
 
 /* Static, human-readable description of a return code. */
 const char* fg_strerror(int code);

@@ -48,11 +48,18 @@ def lib():
         L.fg_force_tile.argtypes = [i, i]
         L.fg_quant_act_1x128.argtypes = [vp, vp, vp, i, i, i, vp]
         L.fg_quant_weight_128x128.argtypes = [vp, vp, vp, i, i, vp]
+        L.fg_gemm_fp8_nt_pow2.argtypes = L.fg_gemm_fp8_nt.argtypes
+        L.fg_grouped_contiguous_pow2.argtypes = L.fg_grouped_contiguous.argtypes
+        L.fg_grouped_masked_pow2.argtypes = L.fg_grouped_masked.argtypes
+        L.fg_quant_act_1x128_pow2.argtypes = L.fg_quant_act_1x128.argtypes
+        L.fg_quant_weight_128x128_pow2.argtypes = L.fg_quant_weight_128x128.argtypes
         L.fg_strerror.argtypes = [i]
         L.fg_strerror.restype = ctypes.c_char_p
         for name in ("fg_gemm_fp8_nt", "fg_grouped_contiguous", "fg_grouped_masked",
                      "fg_select_config", "fg_force_tile", "fg_quant_act_1x128",
-                     "fg_quant_weight_128x128"):
+                     "fg_quant_weight_128x128", "fg_gemm_fp8_nt_pow2", "fg_grouped_contiguous_pow2",
+                     "fg_grouped_masked_pow2", "fg_quant_act_1x128_pow2",
+                     "fg_quant_weight_128x128_pow2"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -101,6 +108,16 @@ def _ptr(t):
 
 def gemm_fp8_nt(A, sa, B, sb, D):
     """Dense D[M, N] = A[M, K] . B[N, K]^T with block scales; writes D in place."""
+    return _dense("fg_gemm_fp8_nt", A, sa, B, sb, D)
+
+
+def gemm_fp8_nt_pow2(A, sa, B, sb, D):
+    """gemm_fp8_nt with power-of-two scales applied by the matrix core (every sa
+    and sb entry must be a power of two in [2^-126, 2^127])."""
+    return _dense("fg_gemm_fp8_nt_pow2", A, sa, B, sb, D)
+
+
+def _dense(fn, A, sa, B, sb, D):
     torch = _torch()
     M, K = A.shape
     N = B.shape[0]
@@ -111,14 +128,23 @@ def gemm_fp8_nt(A, sa, B, sb, D):
     _dev(sa, "sa", (K // 128, M), torch.float32)
     _dev(sb, "sb", (N // 128, K // 128), torch.float32)
     _dev(D, "D", (M, N), torch.bfloat16)
-    _check(lib().fg_gemm_fp8_nt(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D), M, N, K,
-                                _stream(A)), "fg_gemm_fp8_nt")
+    _check(getattr(lib(), fn)(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D), M, N, K,
+                              _stream(A)), fn)
     return D
 
 
 def grouped_contiguous(A, sa, B, sb, D, m_indices):
     """MoE contiguous layout: rows of A belong to expert m_indices[row] (-1 = padding,
     not written); B is [G, N, K]."""
+    return _contiguous("fg_grouped_contiguous", A, sa, B, sb, D, m_indices)
+
+
+def grouped_contiguous_pow2(A, sa, B, sb, D, m_indices):
+    """grouped_contiguous with power-of-two scales applied by the matrix core."""
+    return _contiguous("fg_grouped_contiguous_pow2", A, sa, B, sb, D, m_indices)
+
+
+def _contiguous(fn, A, sa, B, sb, D, m_indices):
     torch = _torch()
     M, K = A.shape
     G, N = B.shape[0], B.shape[1]
@@ -130,15 +156,23 @@ def grouped_contiguous(A, sa, B, sb, D, m_indices):
     _dev(sb, "sb", (G, N // 128, K // 128), torch.float32)
     _dev(D, "D", (M, N), torch.bfloat16)
     _dev(m_indices, "m_indices", (M,), torch.int32)
-    _check(lib().fg_grouped_contiguous(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D),
-                                       _ptr(m_indices), M, N, K, G, _stream(A)),
-           "fg_grouped_contiguous")
+    _check(getattr(lib(), fn)(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D),
+                              _ptr(m_indices), M, N, K, G, _stream(A)), fn)
     return D
 
 
 def grouped_masked(A, sa, B, sb, D, masked_m):
     """MoE masked layout: expert g has masked_m[g] valid rows of A[g]; only those rows
     of D[g] are written. masked_m stays on the device."""
+    return _masked("fg_grouped_masked", A, sa, B, sb, D, masked_m)
+
+
+def grouped_masked_pow2(A, sa, B, sb, D, masked_m):
+    """grouped_masked with power-of-two scales applied by the matrix core."""
+    return _masked("fg_grouped_masked_pow2", A, sa, B, sb, D, masked_m)
+
+
+def _masked(fn, A, sa, B, sb, D, masked_m):
     torch = _torch()
     G, M_max, K = A.shape
     N = B.shape[1]
@@ -150,9 +184,8 @@ def grouped_masked(A, sa, B, sb, D, masked_m):
     _dev(sb, "sb", (G, N // 128, K // 128), torch.float32)
     _dev(D, "D", (G, M_max, N), torch.bfloat16)
     _dev(masked_m, "masked_m", (G,), torch.int32)
-    _check(lib().fg_grouped_masked(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D),
-                                   _ptr(masked_m), G, M_max, N, K, _stream(A)),
-           "fg_grouped_masked")
+    _check(getattr(lib(), fn)(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D),
+                              _ptr(masked_m), G, M_max, N, K, _stream(A)), fn)
     return D
 
 
@@ -172,6 +205,15 @@ def force_tile(bm=0, bn=0):
 def quant_act_1x128(x, q=None, sa=None):
     """fp32 activations [M, K] (or [batch, M, K]) -> (E4M3 codes, sa) with one scale per
     1x128 block; sa comes out in the GEMM's layout [K/128, M] ([batch, K/128, M])."""
+    return _quant_act("fg_quant_act_1x128", x, q, sa)
+
+
+def quant_act_1x128_pow2(x, q=None, sa=None):
+    """quant_act_1x128 with each scale rounded up to a power of two (>= 2^-126)."""
+    return _quant_act("fg_quant_act_1x128_pow2", x, q, sa)
+
+
+def _quant_act(fn, x, q, sa):
     torch = _torch()
     if x.dim() not in (2, 3):
         raise ValueError("x must be [M, K] or [batch, M, K]")
@@ -187,14 +229,22 @@ def quant_act_1x128(x, q=None, sa=None):
         sa = torch.empty(sa_shape, dtype=torch.float32, device=x.device)
     _fp8(q, "q", tuple(x.shape))
     _dev(sa, "sa", sa_shape, torch.float32)
-    _check(lib().fg_quant_act_1x128(_ptr(x), _ptr(q), _ptr(sa), batch, M, K, _stream(x)),
-           "fg_quant_act_1x128")
+    _check(getattr(lib(), fn)(_ptr(x), _ptr(q), _ptr(sa), batch, M, K, _stream(x)), fn)
     return q, sa
 
 
 def quant_weight_128x128(w, q=None, sb=None):
     """fp32 weights [N, K] (or [G, N, K]) -> (E4M3 codes, sb) with one scale per
     128x128 block; sb is [N/128, K/128] ([G, N/128, K/128])."""
+    return _quant_weight("fg_quant_weight_128x128", w, q, sb)
+
+
+def quant_weight_128x128_pow2(w, q=None, sb=None):
+    """quant_weight_128x128 with each scale rounded up to a power of two (>= 2^-126)."""
+    return _quant_weight("fg_quant_weight_128x128_pow2", w, q, sb)
+
+
+def _quant_weight(fn, w, q, sb):
     torch = _torch()
     if w.dim() not in (2, 3):
         raise ValueError("w must be [N, K] or [G, N, K]")
@@ -210,6 +260,5 @@ def quant_weight_128x128(w, q=None, sb=None):
         sb = torch.empty(sb_shape, dtype=torch.float32, device=w.device)
     _fp8(q, "q", tuple(w.shape))
     _dev(sb, "sb", sb_shape, torch.float32)
-    _check(lib().fg_quant_weight_128x128(_ptr(w), _ptr(q), _ptr(sb), rows, K, _stream(w)),
-           "fg_quant_weight_128x128")
+    _check(getattr(lib(), fn)(_ptr(w), _ptr(q), _ptr(sb), rows, K, _stream(w)), fn)
     return q, sb

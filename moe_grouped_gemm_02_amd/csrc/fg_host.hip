@@ -102,25 +102,36 @@ int pick_tile(int layout, int M, int N, int K, int G, int cus) {
   return best;
 }
 
-template <int LAYOUT>
+template <int LAYOUT, bool POW2>
 hipError_t launch_layout(int tile, const Params& p, int grid, hipStream_t s) {
   switch (tile) {
-    case 0: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg0>), dim3(grid), dim3(Cfg0::THREADS), 0, s, p); break;
-    case 1: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg1>), dim3(grid), dim3(Cfg1::THREADS), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg2>), dim3(grid), dim3(Cfg2::THREADS), 0, s, p); break;
-    case 3: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg3>), dim3(grid), dim3(Cfg3::THREADS), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg4>), dim3(grid), dim3(Cfg4::THREADS), 0, s, p); break;
-    case 5: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg5>), dim3(grid), dim3(Cfg5::THREADS), 0, s, p); break;
+    case 0: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg0, POW2>), dim3(grid), dim3(Cfg0::THREADS), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg1, POW2>), dim3(grid), dim3(Cfg1::THREADS), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg2, POW2>), dim3(grid), dim3(Cfg2::THREADS), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg3, POW2>), dim3(grid), dim3(Cfg3::THREADS), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg4, POW2>), dim3(grid), dim3(Cfg4::THREADS), 0, s, p); break;
+    case 5: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg5, POW2>), dim3(grid), dim3(Cfg5::THREADS), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <bool POW2>
+hipError_t launch(int layout, int tile, const Params& p, int grid, hipStream_t s) {
+  switch (layout) {
+    case FG_LAYOUT_DENSE: return launch_layout<fg::kDense, POW2>(tile, p, grid, s);
+    case FG_LAYOUT_CONTIGUOUS: return launch_layout<fg::kContiguous, POW2>(tile, p, grid, s);
+    default: return launch_layout<fg::kMasked, POW2>(tile, p, grid, s);
+  }
+}
+
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// pow2: every sa and sb is a power of two, applied by the matrix core as an
+// E8M0 block scale (no separate promotion)
 int run(int layout, const void* A, const float* sa, const void* B, const float* sb, void* D,
         const int32_t* m_indices, const int32_t* masked_m, int M, int N, int K, int G,
-        hipStream_t stream) {
+        hipStream_t stream, bool pow2) {
   if (M < 0 || N < 0 || K < 128 || (K % 128) != 0 || (N % 128) != 0) return FG_EINVAL;
   if (layout != FG_LAYOUT_DENSE && G < 1) return FG_EINVAL;
   if (M == 0 || N == 0) return FG_OK;
@@ -161,12 +172,7 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   if (tiles > 0x7fffffffL) return FG_EINVAL;
   const int grid = (int)tiles;
 
-  hipError_t e;
-  switch (layout) {
-    case FG_LAYOUT_DENSE: e = launch_layout<fg::kDense>(ti, p, grid, stream); break;
-    case FG_LAYOUT_CONTIGUOUS: e = launch_layout<fg::kContiguous>(ti, p, grid, stream); break;
-    default: e = launch_layout<fg::kMasked>(ti, p, grid, stream); break;
-  }
+  const hipError_t e = pow2 ? launch<true>(layout, ti, p, grid, stream) : launch<false>(layout, ti, p, grid, stream);
   return e == hipSuccess ? FG_OK : FG_ELAUNCH;
 }
 
@@ -176,20 +182,38 @@ extern "C" {
 
 int fg_gemm_fp8_nt(const void* A, const float* sa, const void* B, const float* sb, void* D,
                    int M, int N, int K, hipStream_t stream) {
-  return run(FG_LAYOUT_DENSE, A, sa, B, sb, D, nullptr, nullptr, M, N, K, 1, stream);
+  return run(FG_LAYOUT_DENSE, A, sa, B, sb, D, nullptr, nullptr, M, N, K, 1, stream, false);
 }
 
 int fg_grouped_contiguous(const void* A, const float* sa, const void* B, const float* sb,
                           void* D, const int32_t* m_indices, int M, int N, int K, int G,
                           hipStream_t stream) {
-  return run(FG_LAYOUT_CONTIGUOUS, A, sa, B, sb, D, m_indices, nullptr, M, N, K, G, stream);
+  return run(FG_LAYOUT_CONTIGUOUS, A, sa, B, sb, D, m_indices, nullptr, M, N, K, G, stream, false);
 }
 
 int fg_grouped_masked(const void* A, const float* sa, const void* B, const float* sb,
                       void* D, const int32_t* masked_m, int G, int M_max, int N, int K,
                       hipStream_t stream) {
   if (G < 1) return FG_EINVAL;
-  return run(FG_LAYOUT_MASKED, A, sa, B, sb, D, nullptr, masked_m, M_max, N, K, G, stream);
+  return run(FG_LAYOUT_MASKED, A, sa, B, sb, D, nullptr, masked_m, M_max, N, K, G, stream, false);
+}
+
+int fg_gemm_fp8_nt_pow2(const void* A, const float* sa, const void* B, const float* sb, void* D,
+                        int M, int N, int K, hipStream_t stream) {
+  return run(FG_LAYOUT_DENSE, A, sa, B, sb, D, nullptr, nullptr, M, N, K, 1, stream, true);
+}
+
+int fg_grouped_contiguous_pow2(const void* A, const float* sa, const void* B, const float* sb,
+                               void* D, const int32_t* m_indices, int M, int N, int K, int G,
+                               hipStream_t stream) {
+  return run(FG_LAYOUT_CONTIGUOUS, A, sa, B, sb, D, m_indices, nullptr, M, N, K, G, stream, true);
+}
+
+int fg_grouped_masked_pow2(const void* A, const float* sa, const void* B, const float* sb,
+                           void* D, const int32_t* masked_m, int G, int M_max, int N, int K,
+                           hipStream_t stream) {
+  if (G < 1) return FG_EINVAL;
+  return run(FG_LAYOUT_MASKED, A, sa, B, sb, D, nullptr, masked_m, M_max, N, K, G, stream, true);
 }
 
 int fg_select_config(int layout, int M, int N, int K, int G, int num_cus, int* bm, int* bn,

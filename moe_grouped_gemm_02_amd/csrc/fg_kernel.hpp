@@ -38,6 +38,17 @@
 // activation scale per sub-tile row and its four results form one 8-byte bf16
 // store.
 //
+// Power-of-two variant (POW2). The 2kiu.com DeepGEMM explainer, section 7,
+// points to MX / micro-scaling formats, whose block scales are powers of two
+// (E8M0). gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 applies such a scale per
+// lane -- to that lane's row of each operand and its 32-wide K chunk -- inside
+// the matrix core and adds the result to C. When every sa and sb is a power
+// of two, the scale of a K-block is therefore taken by the MFMA itself: each
+// 16x16 sub-tile accumulates straight into its master accumulator (C = acc),
+// and the partial ring and the VALU promotion disappear. The scales arrive in
+// the same fp32 layout; the exponent field of a normal fp32 power of two is
+// its E8M0 code (bias 127 in both).
+//
 // K order inside a fragment. The hardware sums a 128-long dot product; which
 // lane/byte holds which k does not change the sum as long as both operands use
 // the same placement. Lane l (row l % 16, quarter q = l / 16) holds bytes
@@ -301,12 +312,22 @@ __device__ __forceinline__ f32x4 mfma_e4m3(const i32x8& b_rows, const i32x8& a_r
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b_rows, a_rows, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// acc + 2^(eb-127) * 2^(ea-127) * (B rows . A rows): eb scales the lane's row
+// of the first operand, ea the lane's row of the second
+__device__ __forceinline__ f32x4 mfma_e4m3_pow2(const i32x8& b_rows, const i32x8& a_rows, const f32x4& acc,
+                                               int eb, int ea) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b_rows, a_rows, acc, 0, 0, 0, eb, 0, ea);
+}
+
+// E8M0 code of a positive normal fp32 power of two: its exponent field
+__device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xffu); }
+
 __device__ __forceinline__ void promote(f32x4& acc, const f32x4& part, float s) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(part[r], s, acc[r]);
 }
 
-template <int LAYOUT, class T>
+template <int LAYOUT, class T, bool POW2 = false>
 __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   constexpr int BM = T::BM, BN = T::BN, W = T::W, WM = T::WM, WN = T::WN;
   constexpr int TM = T::TM, TN = T::TN, PD = T::PD, R = T::RING;
@@ -556,6 +577,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   // PL steps still need for the carried promotions.
   i32x8 fbr[R], fa[T::FA2 ? 2 : 1][TM];
   float sc_lo[2][TM], sc_hi[2][TM];
+  int ea[2][TM], eb_lo[2], eb_hi[2];   // POW2: E8M0 codes of the two scale sets
   f32x4 part[P];
   auto scale_read = [&](auto st_c, float (&a)[TM], float& b0, float& b1) {
     constexpr int ST = decltype(st_c)::value;
@@ -567,10 +589,17 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   };
   auto set_scales = [&](auto set_c, const float (&a)[TM], float b0, float b1) {
     constexpr int SET = decltype(set_c)::value;
+    if constexpr (POW2) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      sc_lo[SET][i] = a[i] * b0;
-      sc_hi[SET][i] = T::STRADDLE ? a[i] * b1 : 0.f;
+      for (int i = 0; i < TM; ++i) ea[SET][i] = e8m0_of(a[i]);
+      eb_lo[SET] = e8m0_of(b0);
+      eb_hi[SET] = T::STRADDLE ? e8m0_of(b1) : 0;
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        sc_lo[SET][i] = a[i] * b0;
+        sc_hi[SET][i] = T::STRADDLE ? a[i] * b1 : 0.f;
+      }
     }
   };
   // scale of sub-tile (pi, pj) from scale set SET (a value select: selecting
@@ -613,10 +642,12 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   }
   // before K-block 0 nothing is pending: zero partials promoted with zero
   // scales leave the (zero) accumulators unchanged
+  if constexpr (!POW2) {
 #pragma unroll
-  for (int c = 0; c < P; ++c) part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < P; ++c) part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < TM; ++i) sc_lo[1][i] = sc_hi[1][i] = 0.f;
+    for (int i = 0; i < TM; ++i) sc_lo[1][i] = sc_hi[1][i] = 0.f;
+  }
 
   // promotion of MFMA u - PL of a K-block with phase PH (for u < PL: MFMA
   // STEPS + u - PL of the previous K-block, with the previous scale set)
@@ -669,7 +700,15 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
           static_for<TM>([&](auto ii_c) { fa[NFSET][decltype(ii_c)::value] = fragA(NxtA{}, ii_c); });
         }
       }
-      part[(PH * STEPS + u) % P] = mfma_e4m3(fbr[(PH * TN + j) % R], fa[FSET][i]);
+      if constexpr (POW2) {
+        // this K-block's scales are set PH & 1 (K-blocks alternate sets)
+        constexpr int SET = PH & 1;
+        int eb = eb_lo[SET];
+        if constexpr (T::STRADDLE) eb = j >= j_switch ? eb_hi[SET] : eb_lo[SET];
+        acc[i][j] = mfma_e4m3_pow2(fbr[(PH * TN + j) % R], fa[FSET][i], acc[i][j], eb, ea[SET][i]);
+      } else {
+        part[(PH * STEPS + u) % P] = mfma_e4m3(fbr[(PH * TN + j) % R], fa[FSET][i]);
+      }
       if constexpr (i == 0) {
         // column j+PD of this stage, or (past the end) column j+PD-TN of the next
         constexpr int jn = j + PD;
@@ -688,7 +727,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
             issue(d_c, std::integral_constant<int, TA>{}, std::integral_constant<int, TB>{}, tail);
         }
       });
-      promote_step(ph_c, u_c);
+      if constexpr (!POW2) promote_step(ph_c, u_c);
       step_fence();
     });
     set_scales(std::integral_constant<int, (PH + 1) & 1>{}, sa_next, sb_next0, sb_next1);
@@ -704,7 +743,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   // The last K-block's final PL partials, promoted once after the loop (an
   // exit path per phase that did this work would keep the register allocator
   // from holding each accumulator in one register across the phases).
-  {
+  if constexpr (!POW2) {
     const int last = (KB - 1) % T::UNROLL;
     static_for<T::UNROLL>([&](auto ph_c) {
       constexpr int PH = decltype(ph_c)::value;

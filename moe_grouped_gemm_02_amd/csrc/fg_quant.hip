@@ -9,6 +9,10 @@
 // 128x128 granularity, amax/448 and round-to-nearest-even are the readings
 // taken where the pages stop.
 //
+// The _pow2 entry points round each scale up to a power of two (at least
+// 2^-126), the E8M0 block scales of the MX / micro-scaling formats the 2kiu.com
+// explainer points to in section 7; dividing by such a scale is exact.
+//
 // Inputs must be finite. Both kernels are bandwidth-bound streaming passes:
 // each input byte is read once, each code byte written once.
 #include <hip/hip_runtime.h>
@@ -46,6 +50,17 @@ __device__ __forceinline__ float block_scale(float amax) {
   return amax == 0.0f ? 1.0f : amax / kE4M3Max;   // IEEE division
 }
 
+// Power-of-two variant: the smallest power of two >= s (s positive, finite),
+// and at least 2^-126. A normal s with a zero mantissa is already one;
+// otherwise clear the mantissa and step the exponent up (a subnormal s has
+// exponent field 0 and becomes 2^-126).
+__device__ __forceinline__ float pow2_up(float s) {
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t e = u & 0x7f800000u;
+  if (e != 0u && (u & 0x007fffffu) == 0u) return s;
+  return __uint_as_float(e + 0x00800000u);
+}
+
 __device__ __forceinline__ uint32_t encode4(float4 v, float s) {
   const float lo = -kE4M3Max, hi = kE4M3Max;
   const uint32_t c0 = e4m3_rne(fminf(fmaxf(v.x / s, lo), hi));
@@ -64,7 +79,7 @@ __device__ __forceinline__ float amax4(float4 v) {
 __global__ __launch_bounds__(256) void quant_act_1x128(const float* __restrict__ x,
                                                        uint8_t* __restrict__ q,
                                                        float* __restrict__ sa,
-                                                       int M, int K, long blocks) {
+                                                       int M, int K, long blocks, int pow2) {
   const long blk = (long)blockIdx.x * 8 + (threadIdx.x >> 5);
   if (blk >= blocks) return;
   const int l = threadIdx.x & 31;
@@ -76,7 +91,8 @@ __global__ __launch_bounds__(256) void quant_act_1x128(const float* __restrict__
   float m = amax4(v);
 #pragma unroll
   for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 32));
-  const float s = block_scale(m);
+  float s = block_scale(m);
+  if (pow2) s = pow2_up(s);
   *(uint32_t*)(q + off) = encode4(v, s);
   if (l == 0) {
     const long b = row / M, r = row - b * M;
@@ -88,7 +104,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128(const float* __restrict__
 // w [R][K] (R = G*N rows, a multiple of 128) -> q [R][K], sb [R/128][K/128].
 __global__ __launch_bounds__(256) void quant_weight_128x128(const float* __restrict__ w,
                                                             uint8_t* __restrict__ q,
-                                                            float* __restrict__ sb, int K) {
+                                                            float* __restrict__ sb, int K, int pow2) {
   __shared__ float red[8];
   const int KB = K / 128;
   const long br = blockIdx.x / KB;
@@ -109,7 +125,8 @@ __global__ __launch_bounds__(256) void quant_weight_128x128(const float* __restr
   if ((t & 63) == 0) red[t >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = block_scale(m);
+  float s = block_scale(m);
+  if (pow2) s = pow2_up(s);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const long row = br * 128 + r0 + i * 8;
@@ -120,13 +137,7 @@ __global__ __launch_bounds__(256) void quant_weight_128x128(const float* __restr
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-}  // namespace
-
-extern "C" {
-
-// Declared in fg.h.
-int fg_quant_act_1x128(const float* x, void* q, float* sa, int batch, int M, int K,
-                       hipStream_t stream) {
+int quant_act(const float* x, void* q, float* sa, int batch, int M, int K, hipStream_t stream, int pow2) {
   if (batch < 0 || M < 0 || K < 128 || K % 128) return FG_EINVAL;
   if (batch == 0 || M == 0) return FG_OK;
   if (!x || !q || !sa || !aligned(x, 16) || !aligned(q, 4) || !aligned(sa, 4)) return FG_EINVAL;
@@ -134,20 +145,44 @@ int fg_quant_act_1x128(const float* x, void* q, float* sa, int batch, int M, int
   const long grid = (blocks + 7) / 8;
   if (grid > 0x7fffffffL) return FG_EINVAL;
   hipLaunchKernelGGL(quant_act_1x128, dim3((unsigned)grid), dim3(256), 0, stream, x,
-                     static_cast<uint8_t*>(q), sa, M, K, blocks);
+                     static_cast<uint8_t*>(q), sa, M, K, blocks, pow2);
   return hipGetLastError() == hipSuccess ? FG_OK : FG_ELAUNCH;
 }
 
-int fg_quant_weight_128x128(const float* w, void* q, float* sb, int rows, int K,
-                            hipStream_t stream) {
+int quant_weight(const float* w, void* q, float* sb, int rows, int K, hipStream_t stream, int pow2) {
   if (rows < 0 || rows % 128 || K < 128 || K % 128) return FG_EINVAL;
   if (rows == 0) return FG_OK;
   if (!w || !q || !sb || !aligned(w, 16) || !aligned(q, 4) || !aligned(sb, 4)) return FG_EINVAL;
   const long grid = (long)(rows / 128) * (K / 128);
   if (grid > 0x7fffffffL) return FG_EINVAL;
   hipLaunchKernelGGL(quant_weight_128x128, dim3((unsigned)grid), dim3(256), 0, stream, w,
-                     static_cast<uint8_t*>(q), sb, K);
+                     static_cast<uint8_t*>(q), sb, K, pow2);
   return hipGetLastError() == hipSuccess ? FG_OK : FG_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Declared in fg.h.
+int fg_quant_act_1x128(const float* x, void* q, float* sa, int batch, int M, int K,
+                       hipStream_t stream) {
+  return quant_act(x, q, sa, batch, M, K, stream, 0);
+}
+
+int fg_quant_weight_128x128(const float* w, void* q, float* sb, int rows, int K,
+                            hipStream_t stream) {
+  return quant_weight(w, q, sb, rows, K, stream, 0);
+}
+
+int fg_quant_act_1x128_pow2(const float* x, void* q, float* sa, int batch, int M, int K,
+                            hipStream_t stream) {
+  return quant_act(x, q, sa, batch, M, K, stream, 1);
+}
+
+int fg_quant_weight_128x128_pow2(const float* w, void* q, float* sb, int rows, int K,
+                                 hipStream_t stream) {
+  return quant_weight(w, q, sb, rows, K, stream, 1);
 }
 
 }  // extern "C"

@@ -33,10 +33,11 @@ def new_out(shape, prefill_bits=SENTINEL):
     return D
 
 
-def quant_dense(a, b):
-    """fp32 A [M,K], B [N,K] -> oracle codes/scales in natural layout."""
-    A, sa = oracle.quantize_act_1x128(a)
-    B, sb = oracle.quantize_weight_128x128(b)
+def quant_dense(a, b, pow2=False):
+    """fp32 A [M,K], B [N,K] -> oracle codes/scales in natural layout (pow2:
+    power-of-two scales)."""
+    A, sa = oracle.quantize_act_1x128(a, pow2)
+    B, sb = oracle.quantize_weight_128x128(b, pow2)
     return A, sa, B, sb
 
 
@@ -50,24 +51,43 @@ def masked_inputs(A, sa, B, sb):
     return (to_dev(A), to_dev(np.ascontiguousarray(np.transpose(sa, (0, 2, 1)))), to_dev(B), to_dev(sb))
 
 
-def make_dense(M, N, K, seed, **kw):
+def make_dense(M, N, K, seed, pow2=False, **kw):
     w = workloads.dense(M, N, K, seed, **kw)
-    return quant_dense(w["a"], w["b"])
+    return quant_dense(w["a"], w["b"], pow2)
 
 
-def make_contiguous(G, N, K, seed, **kw):
+def make_contiguous(G, N, K, seed, pow2=False, **kw):
     w = workloads.contiguous(G, N, K, seed, **kw)
-    A, sa = oracle.quantize_act_1x128(w["a"])
-    B, sb = oracle.quantize_weight_128x128(w["b"])
+    A, sa = oracle.quantize_act_1x128(w["a"], pow2)
+    B, sb = oracle.quantize_weight_128x128(w["b"], pow2)
     return A, sa, B, sb, w["m_indices"]
 
 
-def make_masked(G, M_max, N, K, seed, **kw):
+def make_masked(G, M_max, N, K, seed, pow2=False, **kw):
     w = workloads.masked(G, M_max, N, K, seed, **kw)
     Gs = w["a"].shape[0]
     A = np.empty(w["a"].shape, np.uint8)
     sa = np.empty((Gs, M_max, K // 128), np.float32)
     for g in range(Gs):
-        A[g], sa[g] = oracle.quantize_act_1x128(w["a"][g])
-    B, sb = oracle.quantize_weight_128x128(w["b"])
+        A[g], sa[g] = oracle.quantize_act_1x128(w["a"][g], pow2)
+    B, sb = oracle.quantize_weight_128x128(w["b"], pow2)
     return A, sa, B, sb, w["masked_m"]
+
+
+def quant_inputs(shape, seed):
+    """fp32 quantiser inputs with the awkward cases: an outlier row, an all-zero
+    1x128 block, a tiny-valued block, a value that rounds to -0, and exact ties
+    of the E4M3 grid after scaling by amax/448 = 1."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    flat = x.reshape(-1, shape[-1])
+    flat[3] *= 50.0                                   # outlier row
+    flat[5, 128:256] = 0.0                            # all-zero 1x128 block
+    flat[6, :128] = np.float32(2.0 ** -12) * rng.standard_normal(128).astype(np.float32)
+    flat[7, 5] = -1e-30                               # rounds to -0 after scaling
+    flat[8, :128] = 0.0
+    flat[8, 0] = 448.0
+    t = oracle.decode_table()[:0x7F]
+    mids = ((t[:-1] + t[1:]) / 2)
+    flat[8, 1:127] = mids[:126]
+    return x

@@ -23,7 +23,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fg_gemm_fp8_nt", "fg_grouped_contiguous", "fg_grouped_masked",
-              "fg_select_config", "fg_strerror", "fg_quant_act_1x128", "fg_quant_weight_128x128"):
+              "fg_select_config", "fg_strerror", "fg_quant_act_1x128", "fg_quant_weight_128x128",
+              "fg_gemm_fp8_nt_pow2", "fg_grouped_contiguous_pow2", "fg_grouped_masked_pow2",
+              "fg_quant_act_1x128_pow2", "fg_quant_weight_128x128_pow2"):
         assert n in names
 
 
@@ -56,6 +58,7 @@ GOOD = ctypes.c_void_p(0x100000)   # aligned, never dereferenced (validation fai
 ])
 def test_dense_validation(args):
     assert fg.lib().fg_gemm_fp8_nt(*args) == EINVAL
+    assert fg.lib().fg_gemm_fp8_nt_pow2(*args) == EINVAL
 
 
 def test_empty_problems_are_no_ops():
@@ -63,6 +66,8 @@ def test_empty_problems_are_no_ops():
     assert L.fg_gemm_fp8_nt(None, None, None, None, None, 0, 256, 256, None) == OK
     assert L.fg_gemm_fp8_nt(None, None, None, None, None, 64, 0, 256, None) == OK
     assert L.fg_grouped_contiguous(None, None, None, None, None, None, 0, 256, 256, 4, None) == OK
+    assert L.fg_gemm_fp8_nt_pow2(None, None, None, None, None, 0, 256, 256, None) == OK
+    assert L.fg_grouped_masked_pow2(None, None, None, None, None, None, 3, 0, 256, 256, None) == OK
 
 
 def test_grouped_validation():
@@ -76,6 +81,11 @@ def test_grouped_validation():
     # misaligned masked_m
     assert L.fg_grouped_masked(GOOD, GOOD, GOOD, GOOD, GOOD, ctypes.c_void_p(0x100002), 2, 64, 256, 256,
                                None) == EINVAL
+    # the power-of-two entry points validate the same way
+    assert L.fg_grouped_contiguous_pow2(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 64, 256, 256, 0, None) == EINVAL
+    assert L.fg_grouped_contiguous_pow2(GOOD, GOOD, GOOD, GOOD, GOOD, None, 64, 256, 256, 2, None) == EINVAL
+    assert L.fg_grouped_masked_pow2(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 0, 64, 256, 256, None) == EINVAL
+    assert L.fg_grouped_masked_pow2(GOOD, GOOD, GOOD, GOOD, GOOD, None, 2, 64, 256, 256, None) == EINVAL
 
 
 def test_quant_validation():
@@ -84,6 +94,10 @@ def test_quant_validation():
     assert L.fg_quant_act_1x128(BAD, GOOD, GOOD, 1, 64, 128, None) == EINVAL
     assert L.fg_quant_weight_128x128(GOOD, GOOD, GOOD, 100, 128, None) == EINVAL
     assert L.fg_quant_act_1x128(None, None, None, 1, 0, 128, None) == OK
+    assert L.fg_quant_act_1x128_pow2(GOOD, GOOD, GOOD, 1, 64, 100, None) == EINVAL
+    assert L.fg_quant_act_1x128_pow2(BAD, GOOD, GOOD, 1, 64, 128, None) == EINVAL
+    assert L.fg_quant_weight_128x128_pow2(GOOD, GOOD, GOOD, 100, 128, None) == EINVAL
+    assert L.fg_quant_weight_128x128_pow2(None, None, None, 0, 128, None) == OK
 
 
 def test_select_config_fills_the_machine():

@@ -1,5 +1,6 @@
 """Full-size parity: every workload at its real size, in the launch
-configuration the benchmark times (automatic tile choice). The oracle checks
+configuration the benchmark times (automatic tile choice), with fp32 block
+scales and with power-of-two scales on the _pow2 entry points. The oracle checks
 sampled outputs one dot product at a time (spread over the output plus the
 tile edges); rows that must not be written are compared bitwise in full, and
 the whole output must be finite."""
@@ -35,15 +36,18 @@ def assert_all_finite(bits):
     assert not np.any(exp == 0xFF), "NaN/Inf in output"
 
 
-def run_dense_full(name):
+POW2 = pytest.mark.parametrize("pow2", [False, True], ids=["fp32_scales", "pow2_scales"])
+
+
+def run_dense_full(name, pow2):
     w = workloads.make(name)
-    A, sa = oracle.quantize_act_1x128(w["a"])
-    B, sb = oracle.quantize_weight_128x128(w["b"])
+    A, sa = oracle.quantize_act_1x128(w["a"], pow2)
+    B, sb = oracle.quantize_weight_128x128(w["b"], pow2)
     del w
     Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
     M, N = A.shape[0], B.shape[0]
     D = new_out((M, N))
-    fg.gemm_fp8_nt(Ad, sad, Bd, sbd, D)
+    (fg.gemm_fp8_nt_pow2 if pow2 else fg.gemm_fp8_nt)(Ad, sad, Bd, sbd, D)
     torch.cuda.synchronize()
     bits = d_bits(D)
     assert_all_finite(bits)
@@ -55,27 +59,30 @@ def run_dense_full(name):
     assert r["ok"], r
 
 
-def test_fullsize_dense_skinny():
-    print("full dense_skinny 256x7168x7168", flush=True)
-    run_dense_full("dense_skinny")
+@POW2
+def test_fullsize_dense_skinny(pow2):
+    print(f"full dense_skinny 256x7168x7168 pow2={pow2}", flush=True)
+    run_dense_full("dense_skinny", pow2)
 
 
-def test_fullsize_dense_ffn():
-    print("full dense_ffn 8192x7168x18432", flush=True)
-    run_dense_full("dense_ffn")
+@POW2
+def test_fullsize_dense_ffn(pow2):
+    print(f"full dense_ffn 8192x7168x18432 pow2={pow2}", flush=True)
+    run_dense_full("dense_ffn", pow2)
 
 
-def test_fullsize_contiguous():
-    print("full contiguous 8 experts, N=4096, K=7168", flush=True)
+@POW2
+def test_fullsize_contiguous(pow2):
+    print(f"full contiguous 8 experts, N=4096, K=7168 pow2={pow2}", flush=True)
     w = workloads.make("contiguous")
-    A, sa = oracle.quantize_act_1x128(w["a"])
-    B, sb = oracle.quantize_weight_128x128(w["b"])
+    A, sa = oracle.quantize_act_1x128(w["a"], pow2)
+    B, sb = oracle.quantize_weight_128x128(w["b"], pow2)
     mi = w["m_indices"]
     del w
     Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
     M, N = A.shape[0], B.shape[1]
     D = new_out((M, N))
-    fg.grouped_contiguous(Ad, sad, Bd, sbd, D, to_dev(mi))
+    (fg.grouped_contiguous_pow2 if pow2 else fg.grouped_contiguous)(Ad, sad, Bd, sbd, D, to_dev(mi))
     torch.cuda.synchronize()
     bits = d_bits(D)
     valid = mi >= 0
@@ -93,21 +100,22 @@ def test_fullsize_contiguous():
     assert r["ok"], r
 
 
-def test_fullsize_masked():
-    print("full masked 16 experts, M_max=256, N=7168, K=2048", flush=True)
+@POW2
+def test_fullsize_masked(pow2):
+    print(f"full masked 16 experts, M_max=256, N=7168, K=2048 pow2={pow2}", flush=True)
     w = workloads.make("masked")
     G, M_max, K = w["a"].shape
     A = np.empty((G, M_max, K), np.uint8)
     sa = np.empty((G, M_max, K // 128), np.float32)
     for g in range(G):
-        A[g], sa[g] = oracle.quantize_act_1x128(w["a"][g])
-    B, sb = oracle.quantize_weight_128x128(w["b"])
+        A[g], sa[g] = oracle.quantize_act_1x128(w["a"][g], pow2)
+    B, sb = oracle.quantize_weight_128x128(w["b"], pow2)
     mm = w["masked_m"]
     del w
     Ad, sad, Bd, sbd = masked_inputs(A, sa, B, sb)
     N = B.shape[1]
     D = new_out((G, M_max, N))
-    fg.grouped_masked(Ad, sad, Bd, sbd, D, to_dev(mm))
+    (fg.grouped_masked_pow2 if pow2 else fg.grouped_masked)(Ad, sad, Bd, sbd, D, to_dev(mm))
     torch.cuda.synchronize()
     bits = d_bits(D)
     valid = np.arange(M_max)[None, :] < np.clip(mm, 0, M_max)[:, None]

@@ -5,31 +5,14 @@ import torch
 
 import oracle
 import moe_grouped_gemm_02_amd as fg
-from fgtest import to_dev
+from fgtest import quant_inputs, to_dev
 
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(shape, seed):
-    rng = np.random.default_rng(seed)
-    x = rng.standard_normal(shape, dtype=np.float32)
-    flat = x.reshape(-1, shape[-1])
-    flat[3] *= 50.0                                   # outlier row
-    flat[5, 128:256] = 0.0                            # all-zero 1x128 block
-    flat[6, :128] = np.float32(2.0 ** -12) * rng.standard_normal(128).astype(np.float32)
-    flat[7, 5] = -1e-30                               # rounds to -0 after scaling
-    # exact ties of the E4M3 grid after scaling by amax/448 = 1
-    flat[8, :128] = 0.0
-    flat[8, 0] = 448.0
-    t = oracle.decode_table()[:0x7F]
-    mids = ((t[:-1] + t[1:]) / 2)
-    flat[8, 1:127] = mids[:126]
-    return x
-
-
 @pytest.mark.parametrize("shape", [(16, 256), (300, 1024), (3, 40, 384)])
 def test_act_quant_bit_exact(shape):
-    x = _inputs(shape, 7)
+    x = quant_inputs(shape, 7)
     q, sa = fg.quant_act_1x128(to_dev(x))
     torch.cuda.synchronize()
     flat = x.reshape(-1, shape[-1])
