@@ -16,6 +16,9 @@ What it computes (fp64 throughout, numpy):
                  two-level (per 128-wide K-block partial, then scale and add)
                  form the method describes, and single-entry references for
                  sampling full-size outputs.
+  * ``ffn``   -- the fused epilogue of an MoE expert's first projection:
+                 SiLU-gated activation of D (gate/up interleaved in 128-column
+                 blocks), re-quantised with the ``quant`` quantisers.
   * ``check`` -- the acceptance test (per-element and Frobenius bounds, and
                  bitwise "untouched" for rows the call must not write).
 
@@ -44,3 +47,4 @@ from .gemm import (  # noqa: F401
     ref_entries,
 )
 from .check import check, bf16_rne, bf16_bits_to_f64  # noqa: F401
+from .ffn import silu, swiglu_blocks  # noqa: F401
