@@ -22,7 +22,9 @@ host. `per_workload` repeats the measurement for the other workloads (the small
 dense case, MoE contiguous, MoE masked, the large dense FFN GEMM) unless
 --headline-only is given; `per_workload_pow2` measures every workload again on
 the power-of-two-scale entry points (E8M0 scales applied by the matrix core),
-with operands quantised by the power-of-two quantisers.
+with operands quantised by the power-of-two quantisers; `moe_swiglu_quant`
+times the fused first-projection calls (GEMM + SiLU gate + 1x128 E4M3
+re-quantisation, fp32 scales, no activation copy) on the two MoE workloads.
 """
 import argparse
 import ctypes
@@ -39,7 +41,7 @@ if ROOT not in sys.path:
 PEAK_FP8_TFLOPS = 256 * 2.4e9 * 8192 / 1e12    # 5033: 256 CUs x 2.4 GHz x 8192 FLOP/clk/CU
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_02_amd", "csrc", f)
-                  for f in ("fg_kernel.hpp", "fg_host.hip")]
+                  for f in ("fg_kernel.hpp", "fg_e4m3.hpp", "fg_host.hip")]
 PEAK_HBM_GBPS = 8000.0                          # HBM3E, 8 TB/s
 MALL_BYTES = 256 << 20
 HEADLINE = "dense_skinny"
@@ -73,7 +75,7 @@ def parse():
 
 
 # --------------------------------------------------------------------- inputs
-def gpu_operands(name, fg, torch, pow2=False):
+def gpu_operands(name, fg, torch, pow2=False, fused=False):
     """Seeded fp32 inputs (numpy) -> device -> E4M3 + scales by the library's
     quantisers (pow2: the power-of-two-scale quantisers). Returns a dict of
     device tensors and the sizes."""
@@ -91,7 +93,7 @@ def gpu_operands(name, fg, torch, pow2=False):
         A, sa = fg.quant_act_1x128(a)
         B, sb = fg.quant_weight_128x128(b)
     del a, b
-    op = dict(kind=w["kind"], A=A, sa=sa, B=B, sb=sb, pow2=pow2)
+    op = dict(kind=w["kind"], A=A, sa=sa, B=B, sb=sb, pow2=pow2, fused=fused)
     N, K = w["b"].shape[-2], w["b"].shape[-1]
     op.update(N=N, K=K, flop=workloads.useful_flop(w))
     if w["kind"] == "dense":
@@ -111,6 +113,12 @@ def gpu_operands(name, fg, torch, pow2=False):
         op["masked_m"] = torch.from_numpy(w["masked_m"]).to(dev)
         op["D"] = torch.zeros((G, M_max, N), dtype=torch.bfloat16, device=dev)
         op["masked_m_list"] = w["masked_m"].tolist()
+    if fused:
+        # outputs of the fused epilogue instead of D: codes [.., M, N/2], scales [.., N/256, M]
+        lead = op["D"].shape[:-2]
+        M_ = op["D"].shape[-2]
+        op["Q"] = torch.zeros(lead + (M_, N // 2), dtype=torch.uint8, device=dev)
+        op["sq"] = torch.zeros(lead + (N // 256, M_), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     return op
 
@@ -129,6 +137,8 @@ def algorithmic_bytes(op):
     a = rows * K + rows * KB * 4
     b = experts * (N * K + (N // 128) * KB * 4)
     d = rows * N * 2
+    if op.get("fused"):
+        d = rows * (N // 2) + rows * (N // 256) * 4     # E4M3 activation + its 1x128 scales
     return a + b + d
 
 
@@ -155,6 +165,21 @@ def make_step(op, copies, fg, torch):
     sfx = "_pow2" if op["pow2"] else ""
     calls = []
     for c in copies:
+        if op["fused"]:
+            Q, sq, null = P(op["Q"]), P(op["sq"]), ctypes.c_void_p(0)
+            scales = 1 if op["pow2"] else 0
+            if op["kind"] == "dense":
+                args = (P(c["A"]), P(c["sa"]), P(c["B"]), P(c["sb"]), Q, sq, null, M, N, K, scales, stream)
+                calls.append((L.fg_gemm_fp8_nt_swiglu_quant, args))
+            elif op["kind"] == "contiguous":
+                args = (P(c["A"]), P(c["sa"]), P(c["B"]), P(c["sb"]), Q, sq, null, P(op["m_indices"]),
+                        M, N, K, G, scales, stream)
+                calls.append((L.fg_grouped_contiguous_swiglu_quant, args))
+            else:
+                args = (P(c["A"]), P(c["sa"]), P(c["B"]), P(c["sb"]), Q, sq, null, P(op["masked_m"]),
+                        G, M, N, K, scales, stream)
+                calls.append((L.fg_grouped_masked_swiglu_quant, args))
+            continue
         if op["kind"] == "dense":
             args = (P(c["A"]), P(c["sa"]), P(c["B"]), P(c["sb"]), D, M, N, K, stream)
             calls.append((getattr(L, "fg_gemm_fp8_nt" + sfx), args))
@@ -175,8 +200,8 @@ def make_step(op, copies, fg, torch):
     return step
 
 
-def time_workload(name, steps, warmup, fg, torch, pow2=False):
-    op = gpu_operands(name, fg, torch, pow2)
+def time_workload(name, steps, warmup, fg, torch, pow2=False, fused=False):
+    op = gpu_operands(name, fg, torch, pow2, fused)
     copies = replicate(op, torch)
     step = make_step(op, copies, fg, torch)
     for i in range(warmup):
@@ -195,6 +220,8 @@ def time_workload(name, steps, warmup, fg, torch, pow2=False):
     wall_ms = (t1 - t0) * 1e3 / steps
     kern_ms = ev0.elapsed_time(ev1) / steps
     layout = {"dense": 0, "contiguous": 1, "masked": 2}[op["kind"]]
+    if fused:
+        layout |= fg.SELECT_SWIGLU_QUANT
     bm, bn, grid = fg.select_config(layout, op["M"], op["N"], op["K"], op["G"])
     res = dict(op=op, copies=len(copies), wall_ms=wall_ms, kern_ms=kern_ms,
                tile=f"{bm}x{bn}", grid=grid, bytes=algorithmic_bytes(op))
@@ -427,6 +454,16 @@ def main():
             del r
             torch.cuda.empty_cache()
 
+    fused = None
+    if not args.headline_only and not args.no_pow2:
+        fused = {}
+        for name in ("contiguous", "masked"):
+            r = time_workload(name, max(5, args.steps // 2), max(2, args.warmup // 2), fg, torch,
+                              False, True)
+            fused[name] = summarize(r)
+            del r
+            torch.cuda.empty_cache()
+
     if args.calibrate_copy_mb:
         copy_calibration(args.calibrate_copy_mb, torch)
     roof["traffic"] = measured_traffic(args.workload) if not head_pow2 else None
@@ -458,6 +495,7 @@ def main():
         "cpu_baseline": cpu,
         "per_workload": per,
         ("per_workload_fp32" if head_pow2 else "per_workload_pow2"): per_pow2,
+        "moe_swiglu_quant": fused,
     }
     print(json.dumps(line), flush=True)
 

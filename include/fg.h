@@ -53,13 +53,22 @@ enum {
   FG_OK = 0,
   FG_EINVAL = -1,        /* bad argument: null pointer, negative size,
                             K or N not a multiple of 128, misalignment,
-                            G < 1 for a grouped call, unknown tile */
+                            G < 1 for a grouped call, unknown tile
+                            or scale kind; N not a multiple of 256
+                            for the fused calls */
   FG_EUNSUPPORTED = -2,  /* current device is not gfx950 */
   FG_ELAUNCH = -3,       /* the kernel launch failed (hipGetLastError) */
   FG_EDEVICE = -4        /* a HIP runtime query failed */
 };
 
 enum { FG_LAYOUT_DENSE = 0, FG_LAYOUT_CONTIGUOUS = 1, FG_LAYOUT_MASKED = 2 };
+
+/* Block-scale kinds of the fused calls below. */
+enum { FG_SCALES_FP32 = 0, FG_SCALES_POW2 = 1 };
+
+/* OR-ed into fg_select_config's layout: the tile the fused SiLU-gate
+ * epilogue would use. */
+enum { FG_SELECT_SWIGLU_QUANT = 0x100 };
 
 /*
  * Dense ("normal") layout. zwzgs.cn DeepGEMM page, "Features > layouts".
@@ -127,13 +136,55 @@ int fg_grouped_masked_pow2(const void* A, const float* sa, const void* B, const 
                            hipStream_t stream);
 
 /*
+ * Fused first projection of an MoE expert FFN: GEMM, SiLU gate and FP8
+ * re-quantisation in one kernel. The 2kiu.com DeepGEMM explainer, section 7,
+ * names fusing the activation functions around a GEMM, to save memory round
+ * trips, as the next optimisation; sections 4.4 and the zwzgs.cn page
+ * ("Features > fine-grained scaling") give the 1x128 quantisation the next
+ * GEMM consumes. Readings taken (the pages name neither the activation nor a
+ * weight layout): the activation is SiLU-gated, and B's rows interleave gate
+ * and up every 128 rows, so with H = A . B^T as computed by fg_gemm_fp8_nt
+ * (FP32, before bf16 rounding), I = N / 2 and j = 0 .. I/128 - 1,
+ *
+ *     act[m, 128j + c] = silu(H[m, 256j + c]) * H[m, 256j + 128 + c],
+ *     silu(x) = x / (1 + exp(-x))   (FP32),
+ *
+ * and act is quantised per 1x128 block exactly as fg_quant_act_1x128 (scales
+ * = FG_SCALES_FP32) or fg_quant_act_1x128_pow2 (FG_SCALES_POW2) would
+ * quantise it. With FG_SCALES_POW2 the input scales sa, sb must also be
+ * powers of two (as for the fg_*_pow2 calls).
+ *   A, sa, B, sb, m_indices, masked_m, M, M_max, G, K: as for the plain calls.
+ *   N: columns of H, a multiple of 256.
+ *   Q   [M][I] E4M3 (masked [G][M_max][I]), 16-byte aligned: the codes.
+ *   sq  [I/128][M] fp32 (masked [G][I/128][M_max]): the scales, K-block-major
+ *       as the next GEMM's sa (its K is I).
+ *   act [M][I] fp32 (masked [G][M_max][I]), 16-byte aligned, or NULL: the
+ *       activation before quantisation (for callers that keep it, and for
+ *       checking the quantisation bit for bit).
+ * Rows without output (M tail, masked rows >= masked_m[g], contiguous rows
+ * with m_indices = -1) are not written in Q, sq or act. No bf16 H is written.
+ * The call uses 256-column tiles only (fg_select_config with
+ * FG_SELECT_SWIGLU_QUANT); a forced tile of another width gives FG_EINVAL.
+ */
+int fg_gemm_fp8_nt_swiglu_quant(const void* A, const float* sa, const void* B, const float* sb,
+                                void* Q, float* sq, float* act, int M, int N, int K, int scales,
+                                hipStream_t stream);
+int fg_grouped_contiguous_swiglu_quant(const void* A, const float* sa, const void* B, const float* sb,
+                                       void* Q, float* sq, float* act, const int32_t* m_indices,
+                                       int M, int N, int K, int G, int scales, hipStream_t stream);
+int fg_grouped_masked_swiglu_quant(const void* A, const float* sa, const void* B, const float* sb,
+                                   void* Q, float* sq, float* act, const int32_t* masked_m, int G,
+                                   int M_max, int N, int K, int scales, hipStream_t stream);
+
+/*
  * Tile configuration the library would launch for a problem, computed on the
  * host from sizes only (no device access, usable without a GPU). Tiles are
  * chosen from a fixed table to minimise wave quantisation over `num_cus`
  * compute units, the point the zwzgs.cn DeepGEMM page makes in "Technical
  * details > non-standard block sizes" (M=256, N=7168 on 132 SMs: 112 tiles of
  * 128x128 versus 128 of 128x112).
- *   layout  FG_LAYOUT_*; M = total rows (dense, contiguous) or M_max (masked);
+ *   layout  FG_LAYOUT_*, optionally | FG_SELECT_SWIGLU_QUANT;
+ *   M = total rows (dense, contiguous) or M_max (masked);
  *   G = experts (1 for dense). num_cus <= 0 means the library's default (256).
  * Writes the tile's rows/cols to *bm / *bn and the number of workgroups the
  * launch would use to *grid (any of the three may be NULL).

@@ -23,6 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfg.so")
 
 LAYOUT_DENSE, LAYOUT_CONTIGUOUS, LAYOUT_MASKED = 0, 1, 2
+SELECT_SWIGLU_QUANT = 0x100      # fg_select_config: the tile of the fused SiLU-gate epilogue
+SCALES_FP32, SCALES_POW2 = 0, 1
 
 _lib = None
 
@@ -53,13 +55,17 @@ def lib():
         L.fg_grouped_masked_pow2.argtypes = L.fg_grouped_masked.argtypes
         L.fg_quant_act_1x128_pow2.argtypes = L.fg_quant_act_1x128.argtypes
         L.fg_quant_weight_128x128_pow2.argtypes = L.fg_quant_weight_128x128.argtypes
+        L.fg_gemm_fp8_nt_swiglu_quant.argtypes = [vp, fp, vp, fp, vp, fp, fp, i, i, i, i, vp]
+        L.fg_grouped_contiguous_swiglu_quant.argtypes = [vp, fp, vp, fp, vp, fp, fp, ip, i, i, i, i, i, vp]
+        L.fg_grouped_masked_swiglu_quant.argtypes = [vp, fp, vp, fp, vp, fp, fp, ip, i, i, i, i, i, vp]
         L.fg_strerror.argtypes = [i]
         L.fg_strerror.restype = ctypes.c_char_p
         for name in ("fg_gemm_fp8_nt", "fg_grouped_contiguous", "fg_grouped_masked",
                      "fg_select_config", "fg_force_tile", "fg_quant_act_1x128",
                      "fg_quant_weight_128x128", "fg_gemm_fp8_nt_pow2", "fg_grouped_contiguous_pow2",
                      "fg_grouped_masked_pow2", "fg_quant_act_1x128_pow2",
-                     "fg_quant_weight_128x128_pow2"):
+                     "fg_quant_weight_128x128_pow2", "fg_gemm_fp8_nt_swiglu_quant",
+                     "fg_grouped_contiguous_swiglu_quant", "fg_grouped_masked_swiglu_quant"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -187,6 +193,93 @@ def _masked(fn, A, sa, B, sb, D, masked_m):
     _check(getattr(lib(), fn)(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D),
                               _ptr(masked_m), G, M_max, N, K, _stream(A)), fn)
     return D
+
+
+def _fused_outputs(lead, I, M, dev, Q, sq, act, with_act):
+    """Allocate (or check) the fused epilogue's outputs: Q [*lead, M, I] uint8,
+    sq [*lead, I/128, M] fp32, act [*lead, M, I] fp32 or None."""
+    torch = _torch()
+    if Q is None:
+        Q = torch.empty(lead + (M, I), dtype=torch.uint8, device=dev)
+    if sq is None:
+        sq = torch.empty(lead + (I // 128, M), dtype=torch.float32, device=dev)
+    if act is None and with_act:
+        act = torch.empty(lead + (M, I), dtype=torch.float32, device=dev)
+    _fp8(Q, "Q", lead + (M, I))
+    _dev(sq, "sq", lead + (I // 128, M), torch.float32)
+    if act is not None:
+        _dev(act, "act", lead + (M, I), torch.float32)
+    return Q, sq, act
+
+
+def _opt_ptr(t):
+    return ctypes.c_void_p(0) if t is None else _ptr(t)
+
+
+def gemm_fp8_nt_swiglu_quant(A, sa, B, sb, Q=None, sq=None, act=None, pow2=False, with_act=False):
+    """Dense first projection with the fused epilogue: H = A . B^T (B's rows
+    interleave gate and up every 128), act = silu(gate) * up, quantised per 1x128
+    block. Returns (Q [M, N/2] E4M3, sq [N/256, M] fp32, act [M, N/2] fp32 or None).
+    pow2: power-of-two input scales and output scales."""
+    torch = _torch()
+    M, K = A.shape
+    N = B.shape[0]
+    _fp8(A, "A", (M, K))
+    _fp8(B, "B", (N, K))
+    if K % 128 or N % 256:
+        raise ValueError("K must be a multiple of 128 and N of 256")
+    _dev(sa, "sa", (K // 128, M), torch.float32)
+    _dev(sb, "sb", (N // 128, K // 128), torch.float32)
+    Q, sq, act = _fused_outputs((), N // 2, M, A.device, Q, sq, act, with_act)
+    _check(lib().fg_gemm_fp8_nt_swiglu_quant(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(Q), _ptr(sq),
+                                             _opt_ptr(act), M, N, K, int(bool(pow2)), _stream(A)),
+           "fg_gemm_fp8_nt_swiglu_quant")
+    return Q, sq, act
+
+
+def grouped_contiguous_swiglu_quant(A, sa, B, sb, m_indices, Q=None, sq=None, act=None, pow2=False,
+                                    with_act=False):
+    """MoE contiguous first projection with the fused epilogue (see
+    gemm_fp8_nt_swiglu_quant); padding rows (m_indices = -1) are not written."""
+    torch = _torch()
+    M, K = A.shape
+    G, N = B.shape[0], B.shape[1]
+    _fp8(A, "A", (M, K))
+    _fp8(B, "B", (G, N, K))
+    if K % 128 or N % 256:
+        raise ValueError("K must be a multiple of 128 and N of 256")
+    _dev(sa, "sa", (K // 128, M), torch.float32)
+    _dev(sb, "sb", (G, N // 128, K // 128), torch.float32)
+    _dev(m_indices, "m_indices", (M,), torch.int32)
+    Q, sq, act = _fused_outputs((), N // 2, M, A.device, Q, sq, act, with_act)
+    _check(lib().fg_grouped_contiguous_swiglu_quant(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(Q), _ptr(sq),
+                                                    _opt_ptr(act), _ptr(m_indices), M, N, K, G,
+                                                    int(bool(pow2)), _stream(A)),
+           "fg_grouped_contiguous_swiglu_quant")
+    return Q, sq, act
+
+
+def grouped_masked_swiglu_quant(A, sa, B, sb, masked_m, Q=None, sq=None, act=None, pow2=False,
+                                with_act=False):
+    """MoE masked first projection with the fused epilogue; only rows
+    r < masked_m[g] of each expert are written. Q [G, M_max, N/2],
+    sq [G, N/256, M_max], act [G, M_max, N/2]."""
+    torch = _torch()
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    _fp8(A, "A", (G, M_max, K))
+    _fp8(B, "B", (G, N, K))
+    if K % 128 or N % 256:
+        raise ValueError("K must be a multiple of 128 and N of 256")
+    _dev(sa, "sa", (G, K // 128, M_max), torch.float32)
+    _dev(sb, "sb", (G, N // 128, K // 128), torch.float32)
+    _dev(masked_m, "masked_m", (G,), torch.int32)
+    Q, sq, act = _fused_outputs((G,), N // 2, M_max, A.device, Q, sq, act, with_act)
+    _check(lib().fg_grouped_masked_swiglu_quant(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(Q), _ptr(sq),
+                                                _opt_ptr(act), _ptr(masked_m), G, M_max, N, K,
+                                                int(bool(pow2)), _stream(A)),
+           "fg_grouped_masked_swiglu_quant")
+    return Q, sq, act
 
 
 def select_config(layout, M, N, K, G=1, num_cus=0):

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfg.so")
 SOURCES = ["fg_host.hip", "fg_quant.hip"]
-HEADERS = ["fg_kernel.hpp"]
+HEADERS = ["fg_kernel.hpp", "fg_e4m3.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

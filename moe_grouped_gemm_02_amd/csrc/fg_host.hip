@@ -79,16 +79,19 @@ long count_tiles(int layout, int M, int N, int G, const Tile& t) {
 // multiple of the SM count leaves most of the last round idle); partial tiles
 // carry their padding. Contiguous tiles must not straddle an aligned 128-row
 // expert block.
+// The fused SiLU-gate epilogue needs 256-column tiles (one gate and one up
+// block per row); bn256 restricts the choice to those.
 constexpr double kTileFixedCycles = 4000.0;
-int pick_tile(int layout, int M, int N, int K, int G, int cus) {
+int pick_tile(int layout, int M, int N, int K, int G, int cus, bool bn256 = false) {
   const int forced = g_forced_tile.load(std::memory_order_relaxed);
-  if (forced >= 0) return forced;
+  if (forced >= 0) return (!bn256 || kTiles[forced].bn == 256) ? forced : -1;
   int best = -1;
   double best_cost = 0.0;
   const double kblocks = K / 128;
   for (int i = 0; i < kNumTiles; ++i) {
     const Tile& t = kTiles[i];
     if (layout == FG_LAYOUT_CONTIGUOUS && 128 % t.bm != 0) continue;
+    if (bn256 && t.bn != 256) continue;
     const long tiles = count_tiles(layout, M, N, G, t);
     const long rounds = (tiles + cus - 1) / cus;
     const double t_mfma = (double)t.bm * t.bn * 256.0 / (8192.0 * t.eff);
@@ -102,44 +105,69 @@ int pick_tile(int layout, int M, int N, int K, int G, int cus) {
   return best;
 }
 
-template <int LAYOUT, bool POW2>
-hipError_t launch_layout(int tile, const Params& p, int grid, hipStream_t s) {
-  switch (tile) {
-    case 0: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg0, POW2>), dim3(grid), dim3(Cfg0::THREADS), 0, s, p); break;
-    case 1: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg1, POW2>), dim3(grid), dim3(Cfg1::THREADS), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg2, POW2>), dim3(grid), dim3(Cfg2::THREADS), 0, s, p); break;
-    case 3: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg3, POW2>), dim3(grid), dim3(Cfg3::THREADS), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg4, POW2>), dim3(grid), dim3(Cfg4::THREADS), 0, s, p); break;
-    case 5: hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, Cfg5, POW2>), dim3(grid), dim3(Cfg5::THREADS), 0, s, p); break;
-    default: return hipErrorInvalidValue;
+// One tile configuration; the fused epilogue exists only for 256-column tiles.
+template <int LAYOUT, bool POW2, int EPI, class C>
+hipError_t launch_tile(const Params& p, int grid, hipStream_t s) {
+  if constexpr (EPI == fg::kEpiSwigluQuant && C::BN != 256) {
+    return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, C, POW2, EPI>), dim3(grid), dim3(C::THREADS), 0, s, p);
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
-template <bool POW2>
-hipError_t launch(int layout, int tile, const Params& p, int grid, hipStream_t s) {
-  switch (layout) {
-    case FG_LAYOUT_DENSE: return launch_layout<fg::kDense, POW2>(tile, p, grid, s);
-    case FG_LAYOUT_CONTIGUOUS: return launch_layout<fg::kContiguous, POW2>(tile, p, grid, s);
-    default: return launch_layout<fg::kMasked, POW2>(tile, p, grid, s);
+template <int LAYOUT, bool POW2, int EPI>
+hipError_t launch_layout(int tile, const Params& p, int grid, hipStream_t s) {
+  switch (tile) {
+    case 0: return launch_tile<LAYOUT, POW2, EPI, Cfg0>(p, grid, s);
+    case 1: return launch_tile<LAYOUT, POW2, EPI, Cfg1>(p, grid, s);
+    case 2: return launch_tile<LAYOUT, POW2, EPI, Cfg2>(p, grid, s);
+    case 3: return launch_tile<LAYOUT, POW2, EPI, Cfg3>(p, grid, s);
+    case 4: return launch_tile<LAYOUT, POW2, EPI, Cfg4>(p, grid, s);
+    case 5: return launch_tile<LAYOUT, POW2, EPI, Cfg5>(p, grid, s);
+    default: return hipErrorInvalidValue;
   }
 }
+
+template <bool POW2, int EPI>
+hipError_t launch(int layout, int tile, const Params& p, int grid, hipStream_t s) {
+  switch (layout) {
+    case FG_LAYOUT_DENSE: return launch_layout<fg::kDense, POW2, EPI>(tile, p, grid, s);
+    case FG_LAYOUT_CONTIGUOUS: return launch_layout<fg::kContiguous, POW2, EPI>(tile, p, grid, s);
+    default: return launch_layout<fg::kMasked, POW2, EPI>(tile, p, grid, s);
+  }
+}
+
+// Outputs of the fused SiLU-gate + re-quantisation epilogue (all null: the
+// plain bf16 D epilogue).
+struct FusedOut {
+  void* Q = nullptr;
+  float* sq = nullptr;
+  float* act = nullptr;
+};
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // pow2: every sa and sb is a power of two, applied by the matrix core as an
-// E8M0 block scale (no separate promotion)
+// E8M0 block scale (no separate promotion). fused: write the SiLU-gated,
+// re-quantised activation (out.Q / out.sq / out.act) instead of D.
 int run(int layout, const void* A, const float* sa, const void* B, const float* sb, void* D,
         const int32_t* m_indices, const int32_t* masked_m, int M, int N, int K, int G,
-        hipStream_t stream, bool pow2) {
+        hipStream_t stream, bool pow2, const FusedOut* fused = nullptr) {
   if (M < 0 || N < 0 || K < 128 || (K % 128) != 0 || (N % 128) != 0) return FG_EINVAL;
+  if (fused && (N % 256) != 0) return FG_EINVAL;
   if (layout != FG_LAYOUT_DENSE && G < 1) return FG_EINVAL;
   if (M == 0 || N == 0) return FG_OK;
-  if (!A || !sa || !B || !sb || !D) return FG_EINVAL;
+  if (!A || !sa || !B || !sb) return FG_EINVAL;
+  if (fused) {
+    if (!fused->Q || !fused->sq || !aligned(fused->Q, 16) || !aligned(fused->sq, 4)) return FG_EINVAL;
+    if (fused->act && !aligned(fused->act, 16)) return FG_EINVAL;
+  } else if (!D || !aligned(D, 16)) {
+    return FG_EINVAL;
+  }
   if (layout == FG_LAYOUT_CONTIGUOUS && !m_indices) return FG_EINVAL;
   if (layout == FG_LAYOUT_MASKED && !masked_m) return FG_EINVAL;
-  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || !aligned(sa, 4) || !aligned(sb, 4))
-    return FG_EINVAL;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sa, 4) || !aligned(sb, 4)) return FG_EINVAL;
   if (m_indices && !aligned(m_indices, 4)) return FG_EINVAL;
   if (masked_m && !aligned(masked_m, 4)) return FG_EINVAL;
   // the kernels address one expert's A or B with 32-bit byte offsets
@@ -149,7 +177,8 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   const int st = current_device(&cus);
   if (st != FG_OK) return st;
 
-  const int ti = pick_tile(layout, M, N, K, G, cus);
+  const int ti = pick_tile(layout, M, N, K, G, cus, fused != nullptr);
+  if (ti < 0) return FG_EINVAL;   // a forced tile the fused epilogue cannot use
   const Tile& t = kTiles[ti];
   // contiguous tiles must not straddle an aligned 128-row expert block
   if (layout == FG_LAYOUT_CONTIGUOUS && 128 % t.bm != 0) return FG_EINVAL;
@@ -159,6 +188,9 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   p.B = static_cast<const uint8_t*>(B);
   p.sb = sb;
   p.D = static_cast<uint16_t*>(D);
+  p.Q = fused ? static_cast<uint8_t*>(fused->Q) : nullptr;
+  p.sq = fused ? fused->sq : nullptr;
+  p.act = fused ? fused->act : nullptr;
   p.m_indices = m_indices;
   p.masked_m = masked_m;
   p.M = M;
@@ -172,7 +204,13 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   if (tiles > 0x7fffffffL) return FG_EINVAL;
   const int grid = (int)tiles;
 
-  const hipError_t e = pow2 ? launch<true>(layout, ti, p, grid, stream) : launch<false>(layout, ti, p, grid, stream);
+  hipError_t e;
+  if (fused)
+    e = pow2 ? launch<true, fg::kEpiSwigluQuant>(layout, ti, p, grid, stream)
+             : launch<false, fg::kEpiSwigluQuant>(layout, ti, p, grid, stream);
+  else
+    e = pow2 ? launch<true, fg::kEpiBf16>(layout, ti, p, grid, stream)
+             : launch<false, fg::kEpiBf16>(layout, ti, p, grid, stream);
   return e == hipSuccess ? FG_OK : FG_ELAUNCH;
 }
 
@@ -216,13 +254,53 @@ int fg_grouped_masked_pow2(const void* A, const float* sa, const void* B, const 
   return run(FG_LAYOUT_MASKED, A, sa, B, sb, D, nullptr, masked_m, M_max, N, K, G, stream, true);
 }
 
+int fg_gemm_fp8_nt_swiglu_quant(const void* A, const float* sa, const void* B, const float* sb,
+                                void* Q, float* sq, float* act, int M, int N, int K, int scales,
+                                hipStream_t stream) {
+  if (scales != FG_SCALES_FP32 && scales != FG_SCALES_POW2) return FG_EINVAL;
+  FusedOut out;
+  out.Q = Q;
+  out.sq = sq;
+  out.act = act;
+  return run(FG_LAYOUT_DENSE, A, sa, B, sb, nullptr, nullptr, nullptr, M, N, K, 1, stream,
+             scales == FG_SCALES_POW2, &out);
+}
+
+int fg_grouped_contiguous_swiglu_quant(const void* A, const float* sa, const void* B, const float* sb,
+                                       void* Q, float* sq, float* act, const int32_t* m_indices,
+                                       int M, int N, int K, int G, int scales, hipStream_t stream) {
+  if (scales != FG_SCALES_FP32 && scales != FG_SCALES_POW2) return FG_EINVAL;
+  FusedOut out;
+  out.Q = Q;
+  out.sq = sq;
+  out.act = act;
+  return run(FG_LAYOUT_CONTIGUOUS, A, sa, B, sb, nullptr, m_indices, nullptr, M, N, K, G, stream,
+             scales == FG_SCALES_POW2, &out);
+}
+
+int fg_grouped_masked_swiglu_quant(const void* A, const float* sa, const void* B, const float* sb,
+                                   void* Q, float* sq, float* act, const int32_t* masked_m, int G,
+                                   int M_max, int N, int K, int scales, hipStream_t stream) {
+  if (scales != FG_SCALES_FP32 && scales != FG_SCALES_POW2) return FG_EINVAL;
+  if (G < 1) return FG_EINVAL;
+  FusedOut out;
+  out.Q = Q;
+  out.sq = sq;
+  out.act = act;
+  return run(FG_LAYOUT_MASKED, A, sa, B, sb, nullptr, nullptr, masked_m, M_max, N, K, G, stream,
+             scales == FG_SCALES_POW2, &out);
+}
+
 int fg_select_config(int layout, int M, int N, int K, int G, int num_cus, int* bm, int* bn,
                      int* grid) {
+  const bool fused = (layout & FG_SELECT_SWIGLU_QUANT) != 0;
+  layout &= ~FG_SELECT_SWIGLU_QUANT;
   if (layout < FG_LAYOUT_DENSE || layout > FG_LAYOUT_MASKED) return FG_EINVAL;
   if (M < 0 || N < 0 || K < 0 || (layout != FG_LAYOUT_DENSE && G < 1)) return FG_EINVAL;
   if (layout == FG_LAYOUT_DENSE) G = 1;
   const int cus = num_cus > 0 ? num_cus : kDefaultCUs;
-  const int ti = pick_tile(layout, M, N, K, G, cus);
+  const int ti = pick_tile(layout, M, N, K, G, cus, fused);
+  if (ti < 0) return FG_EINVAL;
   if (bm) *bm = kTiles[ti].bm;
   if (bn) *bn = kTiles[ti].bn;
   if (grid) *grid = (int)count_tiles(layout, M, N, G, kTiles[ti]);
@@ -246,7 +324,7 @@ int fg_force_tile(int bm, int bn) {
 const char* fg_strerror(int code) {
   switch (code) {
     case FG_OK: return "success";
-    case FG_EINVAL: return "invalid argument (null pointer, negative size, K or N not a multiple of 128, K < 128, misaligned pointer, G < 1 or unknown tile)";
+    case FG_EINVAL: return "invalid argument (null pointer, negative size, K or N not a multiple of 128 (256 for the fused epilogue), K < 128, misaligned pointer, G < 1, unknown scale kind or tile)";
     case FG_EUNSUPPORTED: return "unsupported device (gfx950 required)";
     case FG_ELAUNCH: return "kernel launch failed";
     case FG_EDEVICE: return "HIP device query failed";

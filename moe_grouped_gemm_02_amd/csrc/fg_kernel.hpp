@@ -38,6 +38,16 @@
 // activation scale per sub-tile row and its four results form one 8-byte bf16
 // store.
 //
+// Fused epilogue (EPI = kEpiSwigluQuant), for an MoE expert's first
+// projection whose weight interleaves gate and up rows every 128: the 2kiu.com
+// explainer, section 7, names fusing the activation around a GEMM as the way
+// to save its memory round trips. A 256-column tile holds gate block j and up
+// block j for its rows; the waves holding the gate half stage silu(gate) in
+// LDS, the up waves form act = silu(gate) * up in FP32 from it and their
+// accumulators, and a 16-lane group per row then takes the row's amax over its
+// 128 columns, the 1x128 scale and 8 codes per lane -- the next GEMM's A operand and its
+// K-block-major scales, with no bf16 D written or re-read.
+//
 // Power-of-two variant (POW2). The 2kiu.com DeepGEMM explainer, section 7,
 // points to MX / micro-scaling formats, whose block scales are powers of two
 // (E8M0). gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 applies such a scale per
@@ -61,6 +71,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "fg_e4m3.hpp"
+
 namespace fg {
 
 typedef int   i32x4 __attribute__((ext_vector_type(4)));
@@ -72,6 +84,9 @@ typedef __attribute__((address_space(1))) const uint8_t gbl_u8;
 typedef __attribute__((address_space(3))) const float lds_f32;
 
 enum Layout { kDense = 0, kContiguous = 1, kMasked = 2 };
+// What the epilogue writes: D in bf16, or the SiLU-gated activation of D
+// re-quantised to E4M3 with 1x128 scales (gate/up interleaved every 128 columns)
+enum Epilogue { kEpiBf16 = 0, kEpiSwigluQuant = 1 };
 
 constexpr int kKBlock = 128;   // scale block along K (elements == bytes)
 constexpr int kXCDs = 8;       // MI355X: workgroups go round-robin to 8 XCDs
@@ -89,6 +104,12 @@ struct Params {
   int N, K, G;
   int KB;                 // K / 128
   int tiles_m, tiles_n;   // tile grid of one group
+  // kEpiSwigluQuant outputs (I = N / 2 columns): codes [rows][I] (masked
+  // [G][M][I]), scales [I/128][rows] (masked [G][I/128][M]), and optionally
+  // the fp32 activation [rows][I] (masked [G][M][I]; null: not written)
+  uint8_t* Q;
+  float* sq;
+  float* act;
 };
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
@@ -322,12 +343,114 @@ __device__ __forceinline__ f32x4 mfma_e4m3_pow2(const i32x8& b_rows, const i32x8
 // E8M0 code of a positive normal fp32 power of two: its exponent field
 __device__ __forceinline__ int e8m0_of(float s) { return (int)((__float_as_uint(s) >> 23) & 0xffu); }
 
+// x * sigmoid(x) in FP32 with the hardware exp2 and reciprocal (about 1e-6
+// relative, far below the error of one E4M3 matrix-core dot product); exp
+// overflows to +inf for very negative x, and x * rcp(inf) gives -0
+__device__ __forceinline__ float silu_f32(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
 __device__ __forceinline__ void promote(f32x4& acc, const f32x4& part, float s) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(part[r], s, acc[r]);
 }
 
-template <int LAYOUT, class T, bool POW2 = false>
+// Fused SiLU-gate + E4M3 re-quantisation epilogue (see the header comment).
+// acc holds this wave's (BM/WGM) x (BN/WGN) block: sub-tile (i, j) row
+// wm*WM + 16i + lr, columns wn*WN + 16j + 4lq + 0..3. Every ring stage is free
+// (the caller has drained the DMAs and passed a barrier).
+template <int LAYOUT, class T, bool POW2>
+__device__ __forceinline__ void swiglu_quant_epilogue(const Params& p, const f32x4 (&acc)[T::TM][T::TN],
+                                                      lds_u8* lds, int g, int m0, int n0, int rows_valid,
+                                                      int wm, int wn, int lr, int lq, int t) {
+  constexpr int BM = T::BM, BN = T::BN, WM = T::WM, WN = T::WN, TM = T::TM, TN = T::TN;
+  static_assert(BN == 256 && 128 % WN == 0, "fused epilogue: 256-column tiles, each wave inside one half");
+  constexpr int UROW = 128 * 4 + 16;   // fp32 row of one 128-column half (+16 B against bank conflicts)
+  static_assert(BM * UROW <= T::LDS_BYTES, "fused epilogue staging exceeds the tile's LDS");
+  constexpr int RPP = T::THREADS / 16;   // rows per pass of the quantiser (16 lanes per row)
+  static_assert(BM % RPP == 0, "every lane takes the same number of rows");
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+  const int M = p.M, I = p.N / 2;
+  const int qc0 = n0 / 2;               // first activation column of this tile
+  uint8_t* Qg = p.Q + (LAYOUT == kMasked ? (size_t)g * M * I : 0);
+  float* sqg = p.sq + (LAYOUT == kMasked ? (size_t)g * (I / 128) * M : 0);
+  float* actg = p.act ? p.act + (LAYOUT == kMasked ? (size_t)g * M * I : 0) : nullptr;
+  auto row_ok = [&](int m) {
+    bool ok = m < rows_valid;
+    if (LAYOUT == kContiguous && ok) ok = p.m_indices[m] == g;
+    return ok;
+  };
+
+  // Gate waves store silu(gate) in LDS [BM][128] fp32; after the barrier the
+  // up waves form act = silu(gate) * up in place (and write act if asked).
+  // (Staging the raw up accumulators instead makes the register allocator
+  // spill the main loop's DMA offsets in the FP32-scale instantiations.) One
+  // sub-tile row of LDS reads at a time in the second pass: hoisting all of
+  // them would keep TM*TN more fragments live next to the accumulators.
+  const bool up_wave = wn * WN >= 128;
+  if (!up_wave) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int ml = wm * WM + i * 16 + lr, c = wn * WN + j * 16 + 4 * lq;
+        f32x4 sg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sg[r] = silu_f32(acc[i][j][r]);
+        *(lds_f32x4*)(lds + ml * UROW + c * 4) = sg;
+      }
+  }
+  wait_lgkm0();
+  block_barrier();
+  if (up_wave) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int ml = wm * WM + i * 16 + lr, c = wn * WN - 128 + j * 16 + 4 * lq;
+        lds_f32x4* at = (lds_f32x4*)(lds + ml * UROW + c * 4);
+        const f32x4 sg = *at;
+        f32x4 a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] = sg[r] * acc[i][j][r];
+        *at = a;
+        if (actg) {
+          const int m = m0 + ml;
+          if (row_ok(m)) *(f32x4*)(actg + (size_t)m * I + qc0 + c) = a;
+        }
+        if (j == TN - 1) __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+  wait_lgkm0();
+  block_barrier();
+  // quantise: a 16-lane group per row, 8 columns per lane
+  const int c8 = (t & 15) * 8;
+  const size_t kbq = (size_t)(qc0 / 128);
+#pragma unroll 2
+  for (int rr = t >> 4; rr < BM; rr += RPP) {
+    const lds_f32x4* at = (const lds_f32x4*)(lds + rr * UROW + c8 * 4);
+    const f32x4 v0 = at[0], v1 = at[1];
+    float am = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) am = fmaxf(am, fmaxf(fabsf(v0[r]), fabsf(v1[r])));
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) am = fmaxf(am, __shfl_xor(am, d, 16));
+    float s = block_scale(am);
+    if constexpr (POW2) s = pow2_up(s);
+    const uint32_t lo = e4m3_scaled(v0[0], s) | (e4m3_scaled(v0[1], s) << 8) | (e4m3_scaled(v0[2], s) << 16) |
+                        (e4m3_scaled(v0[3], s) << 24);
+    const uint32_t hi = e4m3_scaled(v1[0], s) | (e4m3_scaled(v1[1], s) << 8) | (e4m3_scaled(v1[2], s) << 16) |
+                        (e4m3_scaled(v1[3], s) << 24);
+    const int m = m0 + rr;
+    if (row_ok(m)) {
+      *(u32x2*)(Qg + (size_t)m * I + qc0 + c8) = u32x2{lo, hi};
+      if ((t & 15) == 0) sqg[kbq * M + m] = s;
+    }
+  }
+}
+
+template <int LAYOUT, class T, bool POW2 = false, int EPI = kEpiBf16>
 __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   constexpr int BM = T::BM, BN = T::BN, W = T::W, WM = T::WM, WN = T::WN;
   constexpr int TM = T::TM, TN = T::TN, PD = T::PD, R = T::RING;
@@ -759,11 +882,15 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   }
 
 
-  // ---- epilogue: bf16 RNE, staged through LDS so that every global store is
-  // a full 16-byte piece of a contiguous output row
   wait_vm<0>();          // the clamped tail DMAs must land before LDS is reused
   wait_lgkm0();
   block_barrier();
+  if constexpr (EPI == kEpiSwigluQuant) {
+    swiglu_quant_epilogue<LAYOUT, T, POW2>(p, acc, lds, g, m0, n0, rows_valid, wm, wn, lr, lq, t);
+    return;
+  }
+  // ---- epilogue: bf16 RNE, staged through LDS so that every global store is
+  // a full 16-byte piece of a contiguous output row
   constexpr int ROWB = T::ROWB;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {

@@ -20,54 +20,17 @@
 #include <cstdint>
 
 #include "fg.h"
+#include "fg_e4m3.hpp"
 
 namespace {
 
-constexpr float kE4M3Max = 448.0f;
-
-// Nearest E4M3 code of y (|y| <= 448, finite), ties to the even code; the
-// sign bit is copied from y.
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
-  const uint32_t bits = __float_as_uint(y);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = __uint_as_float(bits & 0x7fffffffu);
-  uint32_t mag;
-  if (a < 0.015625f) {
-    // below the smallest normal 2^-6 the codes 0..8 are the multiples
-    // c * 2^-9; a * 512 is exact, rintf rounds half to even
-    mag = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    // keep 3 mantissa bits: round the fp32 significand at bit 20, half to even
-    uint32_t u = bits & 0x7fffffffu;
-    u += 0x7ffffu + ((u >> 20) & 1u);
-    const uint32_t e = (u >> 23) - 127u + 7u;  // E4M3 exponent field (1..15)
-    mag = (e << 3) | ((u >> 20) & 7u);
-  }
-  return sign | mag;
-}
-
-__device__ __forceinline__ float block_scale(float amax) {
-  return amax == 0.0f ? 1.0f : amax / kE4M3Max;   // IEEE division
-}
-
-// Power-of-two variant: the smallest power of two >= s (s positive, finite),
-// and at least 2^-126. A normal s with a zero mantissa is already one;
-// otherwise clear the mantissa and step the exponent up (a subnormal s has
-// exponent field 0 and becomes 2^-126).
-__device__ __forceinline__ float pow2_up(float s) {
-  const uint32_t u = __float_as_uint(s);
-  const uint32_t e = u & 0x7f800000u;
-  if (e != 0u && (u & 0x007fffffu) == 0u) return s;
-  return __uint_as_float(e + 0x00800000u);
-}
+using fg::block_scale;
+using fg::e4m3_scaled;
+using fg::pow2_up;
 
 __device__ __forceinline__ uint32_t encode4(float4 v, float s) {
-  const float lo = -kE4M3Max, hi = kE4M3Max;
-  const uint32_t c0 = e4m3_rne(fminf(fmaxf(v.x / s, lo), hi));
-  const uint32_t c1 = e4m3_rne(fminf(fmaxf(v.y / s, lo), hi));
-  const uint32_t c2 = e4m3_rne(fminf(fmaxf(v.z / s, lo), hi));
-  const uint32_t c3 = e4m3_rne(fminf(fmaxf(v.w / s, lo), hi));
-  return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  return e4m3_scaled(v.x, s) | (e4m3_scaled(v.y, s) << 8) | (e4m3_scaled(v.z, s) << 16) |
+         (e4m3_scaled(v.w, s) << 24);
 }
 
 __device__ __forceinline__ float amax4(float4 v) {

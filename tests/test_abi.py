@@ -25,7 +25,9 @@ def test_header_declares_the_entry_points():
     for n in ("fg_gemm_fp8_nt", "fg_grouped_contiguous", "fg_grouped_masked",
               "fg_select_config", "fg_strerror", "fg_quant_act_1x128", "fg_quant_weight_128x128",
               "fg_gemm_fp8_nt_pow2", "fg_grouped_contiguous_pow2", "fg_grouped_masked_pow2",
-              "fg_quant_act_1x128_pow2", "fg_quant_weight_128x128_pow2"):
+              "fg_quant_act_1x128_pow2", "fg_quant_weight_128x128_pow2",
+              "fg_gemm_fp8_nt_swiglu_quant", "fg_grouped_contiguous_swiglu_quant",
+              "fg_grouped_masked_swiglu_quant"):
         assert n in names
 
 
@@ -98,6 +100,32 @@ def test_quant_validation():
     assert L.fg_quant_act_1x128_pow2(BAD, GOOD, GOOD, 1, 64, 128, None) == EINVAL
     assert L.fg_quant_weight_128x128_pow2(GOOD, GOOD, GOOD, 100, 128, None) == EINVAL
     assert L.fg_quant_weight_128x128_pow2(None, None, None, 0, 128, None) == OK
+
+
+def test_fused_validation():
+    L = fg.lib()
+    # N not a multiple of 256, unknown scale kind, null or misaligned outputs
+    assert L.fg_gemm_fp8_nt_swiglu_quant(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, 64, 384, 256, 0, None) == EINVAL
+    assert L.fg_gemm_fp8_nt_swiglu_quant(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, 64, 512, 256, 2, None) == EINVAL
+    assert L.fg_gemm_fp8_nt_swiglu_quant(GOOD, GOOD, GOOD, GOOD, None, GOOD, None, 64, 512, 256, 0, None) == EINVAL
+    assert L.fg_gemm_fp8_nt_swiglu_quant(GOOD, GOOD, GOOD, GOOD, GOOD, None, None, 64, 512, 256, 0, None) == EINVAL
+    assert L.fg_gemm_fp8_nt_swiglu_quant(GOOD, GOOD, GOOD, GOOD, BAD, GOOD, None, 64, 512, 256, 0, None) == EINVAL
+    assert L.fg_gemm_fp8_nt_swiglu_quant(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, BAD, 64, 512, 256, 0, None) == EINVAL
+    assert L.fg_grouped_contiguous_swiglu_quant(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, None, 64, 512, 256, 2,
+                                                0, None) == EINVAL
+    assert L.fg_grouped_masked_swiglu_quant(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None, GOOD, 0, 64, 512, 256,
+                                            0, None) == EINVAL
+    # empty problems launch nothing
+    assert L.fg_gemm_fp8_nt_swiglu_quant(None, None, None, None, None, None, None, 0, 512, 256, 0, None) == OK
+
+
+def test_fused_select_config_uses_256_column_tiles():
+    for layout, M, N, K, G in [(0, 256, 7168, 7168, 1), (0, 8192, 7168, 18432, 1), (1, 9472, 4096, 7168, 8),
+                               (2, 256, 7168, 2048, 16), (0, 64, 512, 256, 1)]:
+        bm, bn, grid = fg.select_config(layout | fg.SELECT_SWIGLU_QUANT, M, N, K, G)
+        assert bn == 256
+        if layout == 1:
+            assert 128 % bm == 0
 
 
 def test_select_config_fills_the_machine():
