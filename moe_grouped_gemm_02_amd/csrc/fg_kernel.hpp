@@ -437,11 +437,16 @@ __device__ __forceinline__ void swiglu_quant_epilogue(const Params& p, const f32
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) am = fmaxf(am, __shfl_xor(am, d, 16));
     float s = block_scale(am);
-    if constexpr (POW2) s = pow2_up(s);
-    const uint32_t lo = e4m3_scaled(v0[0], s) | (e4m3_scaled(v0[1], s) << 8) | (e4m3_scaled(v0[2], s) << 16) |
-                        (e4m3_scaled(v0[3], s) << 24);
-    const uint32_t hi = e4m3_scaled(v1[0], s) | (e4m3_scaled(v1[1], s) << 8) | (e4m3_scaled(v1[2], s) << 16) |
-                        (e4m3_scaled(v1[3], s) << 24);
+    uint32_t lo, hi;
+    if constexpr (POW2) {
+      s = pow2_up(s);
+      const float inv = 1.0f / s;   // exact: s is a power of two
+      lo = e4m3x4_mul(v0[0], v0[1], v0[2], v0[3], inv);
+      hi = e4m3x4_mul(v1[0], v1[1], v1[2], v1[3], inv);
+    } else {
+      lo = e4m3x4_div(v0[0], v0[1], v0[2], v0[3], s);
+      hi = e4m3x4_div(v1[0], v1[1], v1[2], v1[3], s);
+    }
     const int m = m0 + rr;
     if (row_ok(m)) {
       *(u32x2*)(Qg + (size_t)m * I + qc0 + c8) = u32x2{lo, hi};
@@ -462,7 +467,11 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = uniform(t >> 6);
-  const int wm = wave / T::WGN, wn = wave % T::WGN;
+  // Waves w and w+4 share a SIMD. The fused epilogue gives the gate and the
+  // up half of the tile different work, so there the column half is the high
+  // part of the wave number and every SIMD holds one wave of each half.
+  const int wm = EPI == kEpiSwigluQuant ? wave % T::WGM : wave / T::WGN;
+  const int wn = EPI == kEpiSwigluQuant ? wave / T::WGM : wave % T::WGN;
   const int lr = lane & 15, lq = lane >> 4;
 
   // ---- workgroup -> tile. Consecutive tile ids are placed on the same XCD

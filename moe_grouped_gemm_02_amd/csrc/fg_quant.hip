@@ -25,12 +25,12 @@
 namespace {
 
 using fg::block_scale;
-using fg::e4m3_scaled;
 using fg::pow2_up;
 
-__device__ __forceinline__ uint32_t encode4(float4 v, float s) {
-  return e4m3_scaled(v.x, s) | (e4m3_scaled(v.y, s) << 8) | (e4m3_scaled(v.z, s) << 16) |
-         (e4m3_scaled(v.w, s) << 24);
+// Four codes of a block with scale s (pow2: s is a power of two and the
+// division is a multiplication by its exact reciprocal).
+__device__ __forceinline__ uint32_t encode4(float4 v, float s, int pow2) {
+  return pow2 ? fg::e4m3x4_mul(v.x, v.y, v.z, v.w, 1.0f / s) : fg::e4m3x4_div(v.x, v.y, v.z, v.w, s);
 }
 
 __device__ __forceinline__ float amax4(float4 v) {
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128(const float* __restrict__
   for (int d = 16; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 32));
   float s = block_scale(m);
   if (pow2) s = pow2_up(s);
-  *(uint32_t*)(q + off) = encode4(v, s);
+  *(uint32_t*)(q + off) = encode4(v, s, pow2);
   if (l == 0) {
     const long b = row / M, r = row - b * M;
     sa[(b * KB + kb) * (long)M + r] = s;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void quant_weight_128x128(const float* __restr
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const long row = br * 128 + r0 + i * 8;
-    *(uint32_t*)(q + row * K + (long)kb * 128 + col) = encode4(v[i], s);
+    *(uint32_t*)(q + row * K + (long)kb * 128 + col) = encode4(v[i], s, pow2);
   }
   if (t == 0) sb[br * KB + kb] = s;
 }

@@ -37,3 +37,36 @@ def test_weight_quant_bit_exact(shape):
     codes, scales = oracle.quantize_weight_128x128(w)
     assert np.array_equal(q.cpu().numpy(), codes)
     assert np.array_equal(sb.cpu().numpy(), scales)
+
+
+def boundary_rows():
+    """Rows of 128 values whose block maximum is exactly 448 (scale 1, or 2^0 for
+    power-of-two scales), so every code is the encoder's own rounding decision:
+    every finite E4M3 value, every midpoint between neighbours, and the fp32
+    values just below and above each midpoint, with both signs."""
+    t = oracle.decode_table()[:0x7F].astype(np.float64)          # 0 .. 448, ascending
+    mids = (t[:-1] + t[1:]) / 2
+    vals = np.concatenate([t, mids,
+                           np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+                           [2.0 ** -10, 3 * 2.0 ** -11, 1e-30, 2.0 ** -126, 1e-45]]).astype(np.float32)
+    vals = np.concatenate([vals, -vals])
+    per_row = 127
+    rows = -(-vals.size // per_row)
+    x = np.zeros((rows, 128), np.float32)
+    for r in range(rows):
+        chunk = vals[r * per_row:(r + 1) * per_row]
+        x[r, :chunk.size] = chunk
+        x[r, 127] = 448.0
+    return x
+
+
+@pytest.mark.parametrize("pow2", [False, True], ids=["fp32_scales", "pow2_scales"])
+def test_quant_rounding_boundaries_bit_exact(pow2):
+    x = boundary_rows()
+    q, sa = (fg.quant_act_1x128_pow2 if pow2 else fg.quant_act_1x128)(to_dev(x))
+    torch.cuda.synchronize()
+    codes, scales = oracle.quantize_act_1x128(x, pow2)
+    assert np.all(scales == 1.0)
+    assert np.array_equal(sa.cpu().numpy().T, scales)
+    assert np.array_equal(q.cpu().numpy(), codes)
