@@ -575,7 +575,9 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
     rsS[q] = is_b ? rsSB : rsSA;
     sc_stride[q] = is_b ? 4u : (uint32_t)M * 4u;
     sc_dst[q] = lds_addr + T::SC_BASE + (is_b ? BM * 4 : i * 256);
-    sc_off[q] = is_b ? (uint32_t)min(nb_tile + lane, p.N / 128 - 1) * (uint32_t)KB * 4u
+    // weight scales: a tile reads at most the blocks nb_tile .. nb_tile+2, so
+    // lanes past 3 repeat lane 3's row (one cache line instead of one per lane)
+    sc_off[q] = is_b ? (uint32_t)min(nb_tile + min(lane, 3), p.N / 128 - 1) * (uint32_t)KB * 4u
                      : (uint32_t)min(m0 + i * 64 + lane, M - 1) * 4u;
   }
   const uint32_t wave_at = lds_addr + wave * 1024;   // this wave's 1 KB DMA slot in a tile region
