@@ -51,9 +51,11 @@ using Cfg2 = fg::TileCfg<128, 256, 2, 4, 3, false, 2, false, 3>;   // contiguous
 using Cfg3 = fg::TileCfg<128, 128, 2, 2, 4, false, 3, false, 3>;
 using Cfg4 = fg::TileCfg<64, 112, 4, 1, 6, true, 6, true, 3, 3>;     // skinny M, HBM-bound
 using Cfg5 = fg::TileCfg<256, 112, 4, 1, 3, true, 2, false, 3>;    // masked decode, HBM-bound
+using Cfg6 = fg::TileCfg<256, 224, 4, 2, 2, true, 2, false, 3>;    // N = 7168: 32 column tiles
 constexpr Tile kTiles[] = {{256, 256, Cfg0::W, 0.70}, {256, 128, Cfg1::W, 0.75},
                            {128, 256, Cfg2::W, 0.75}, {128, 128, Cfg3::W, 0.70},
-                           {64, 112, Cfg4::W, 0.60},  {256, 112, Cfg5::W, 0.70}};
+                           {64, 112, Cfg4::W, 0.60},  {256, 112, Cfg5::W, 0.70},
+                           {256, 224, Cfg6::W, 0.70}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kDefaultCUs = 256;
 
@@ -125,6 +127,7 @@ hipError_t launch_layout(int tile, const Params& p, int grid, hipStream_t s) {
     case 3: return launch_tile<LAYOUT, POW2, EPI, Cfg3>(p, grid, s);
     case 4: return launch_tile<LAYOUT, POW2, EPI, Cfg4>(p, grid, s);
     case 5: return launch_tile<LAYOUT, POW2, EPI, Cfg5>(p, grid, s);
+    case 6: return launch_tile<LAYOUT, POW2, EPI, Cfg6>(p, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

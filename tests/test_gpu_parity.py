@@ -142,7 +142,7 @@ def test_masked_nan_rows_beyond_count_do_not_leak():
     assert r["ok"], r
 
 
-TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (64, 112), (256, 112)]
+TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (64, 112), (256, 112), (256, 224)]
 
 
 @pytest.fixture
@@ -207,10 +207,11 @@ def test_every_tile_fewer_kblocks_than_stages(forced_tile, K):
 
 
 @pytest.mark.parametrize("forced_tile,kblocks",
-                         [((64, 112), kb) for kb in range(1, 14)] + [((256, 256), kb) for kb in range(1, 8)],
+                         [((64, 112), kb) for kb in range(1, 14)] + [((256, 256), kb) for kb in range(1, 8)]
+                         + [((256, 224), kb) for kb in range(1, 8)],
                          indirect=["forced_tile"], ids=lambda v: f"{v[0]}x{v[1]}" if isinstance(v, tuple) else f"kb{v}")
 def test_every_loop_exit_phase(forced_tile, kblocks):
-    """The K loop is unrolled over 12 (64x112) or 6 (256x256) K-blocks and
+    """The K loop is unrolled over 12 (64x112) or 6 (256x256, 256x224) K-blocks and
     finishes the last partials in a branch per exit phase; these K lengths
     end the loop in every phase."""
     K = 128 * kblocks

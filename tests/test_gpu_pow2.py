@@ -14,7 +14,7 @@ from fgtest import (SENTINEL, d_bits, dense_inputs, make_contiguous, make_dense,
 
 pytestmark = pytest.mark.gpu
 
-TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (64, 112), (256, 112)]
+TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (64, 112), (256, 112), (256, 224)]
 
 
 @pytest.fixture
