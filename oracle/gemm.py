@@ -24,7 +24,9 @@ master accumulator. That is the same sum regrouped, so both forms agree up to
 rounding; ``ref_dense_twolevel`` keeps the pages' order for comparison.
 
 Scale layouts here are the natural ones: sa [M, K/128] (row-major), sb
-[N/128, K/128]. Grouped weights are [G, N, K] with sb [G, N/128, K/128].
+[ceil(N/128), K/128]. Grouped weights are [G, N, K] with sb [G, ceil(N/128), K/128].
+N need not be a multiple of 128: the last weight-scale block then covers the
+remaining N mod 128 rows.
 
 Readings for the grouped layouts (the pages name them only):
   * contiguous: rows of all experts are concatenated along M; m_indices[m] is
@@ -49,10 +51,12 @@ def dequant_act(codes, sa):
 
 
 def dequant_weight(codes, sb):
-    """Bhat = dec(codes) * sb broadcast over each 128x128 block (fp64)."""
+    """Bhat = dec(codes) * sb broadcast over each 128x128 block (fp64); N rows need
+    not fill the last block (sb has ceil(N/128) rows)."""
     codes = np.asarray(codes, dtype=np.uint8)
     sb = np.asarray(sb, dtype=np.float32).astype(np.float64)
-    return _DEC[codes] * np.repeat(np.repeat(sb, 128, axis=-2), 128, axis=-1)
+    N = codes.shape[-2]
+    return _DEC[codes] * np.repeat(np.repeat(sb, 128, axis=-2), 128, axis=-1)[..., :N, :]
 
 
 def ref_dense(A, sa, B, sb):
@@ -71,7 +75,7 @@ def ref_dense_twolevel(A, sa, B, sb):
     N = B.shape[0]
     sa = np.asarray(sa, dtype=np.float32).astype(np.float64)
     sb = np.asarray(sb, dtype=np.float32).astype(np.float64)
-    sb_cols = np.repeat(sb, 128, axis=0)            # [N, K/128]
+    sb_cols = np.repeat(sb, 128, axis=0)[:N]        # [N, K/128]
     acc = np.zeros((M, N), dtype=np.float64)
     for kb in range(K // 128):
         ks = slice(kb * 128, (kb + 1) * 128)

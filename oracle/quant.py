@@ -73,14 +73,30 @@ def quantize_act_1x128(x, pow2=False):
     return quantize_blocks(x, 1, 128, pow2)
 
 
+def _quantize_weight_2d(w, pow2):
+    """128x128 blocks of w [N, K]; when N is not a multiple of 128 the last row
+    block holds the remaining N mod 128 rows (reading: its amax and scale come
+    from those rows alone). Zero rows appended to fill the block change neither
+    its amax nor its scale, so the block is quantised padded and cut back."""
+    N, K = w.shape
+    Np = -(-N // 128) * 128
+    if Np == N:
+        return quantize_blocks(w, 128, 128, pow2)
+    wp = np.zeros((Np, K), dtype=np.float32)
+    wp[:N] = w
+    codes, scale = quantize_blocks(wp, 128, 128, pow2)
+    return codes[:N], scale
+
+
 def quantize_weight_128x128(w, pow2=False):
-    """Weight quantisation: w fp32 [N, K] (or [G, N, K]) -> codes, sb [N/128, K/128]
-    (or [G, N/128, K/128])."""
+    """Weight quantisation: w fp32 [N, K] (or [G, N, K]) -> codes, sb [ceil(N/128), K/128]
+    (or [G, ceil(N/128), K/128])."""
     w = np.asarray(w, dtype=np.float32)
     if w.ndim == 2:
-        return quantize_blocks(w, 128, 128, pow2)
+        return _quantize_weight_2d(w, pow2)
+    nb = -(-w.shape[1] // 128)
     codes = np.empty(w.shape, dtype=np.uint8)
-    scales = np.empty((w.shape[0], w.shape[1] // 128, w.shape[2] // 128), dtype=np.float32)
+    scales = np.empty((w.shape[0], nb, w.shape[2] // 128), dtype=np.float32)
     for g in range(w.shape[0]):
-        codes[g], scales[g] = quantize_blocks(w[g], 128, 128, pow2)
+        codes[g], scales[g] = _quantize_weight_2d(w[g], pow2)
     return codes, scales
