@@ -27,9 +27,15 @@
  *     allocates no device memory and keeps no reference after returning.
  *   - A, B: E4M3 bytes, K contiguous ("NT": B is given as N x K).
  *   - sa: fp32, K-block-major: sa[kb * M + m] (masked: [G][K/128][M_max]).
- *   - sb: fp32, row-major [N/128][K/128] (grouped: [G][N/128][K/128]).
+ *   - sb: fp32, row-major [ceil(N/128)][K/128] (grouped: [G][ceil(N/128)][K/128]);
+ *     when N is not a multiple of 128 the last row block of B covers the
+ *     remaining N mod 128 rows.
  *   - D: bf16 bit patterns, row-major [M][N] (masked: [G][M_max][N]).
- *   - K and N must be multiples of 128; M is arbitrary (>= 0).
+ *   - K must be a multiple of 128 and N a multiple of 8 (whole 16-byte pieces
+ *     of a bf16 output row; the fused calls need N % 256 == 0); M is
+ *     arbitrary (>= 0). The boundary handling the 2kiu.com explainer
+ *     discusses in section 4.3 is done in one code path: loads past N are
+ *     clamped to row N-1 and the stores of columns >= N are skipped.
  *   - A, B and D base pointers must be 16-byte aligned, sa and sb 4-byte.
  *   - Calls are asynchronous on `stream` (0 = null stream), never synchronise
  *     and never read device data on the host, so they can be captured in a
@@ -52,7 +58,8 @@ extern "C" {
 enum {
   FG_OK = 0,
   FG_EINVAL = -1,        /* bad argument: null pointer, negative size,
-                            K or N not a multiple of 128, misalignment,
+                            K not a multiple of 128, N not a multiple of
+                            8, misalignment,
                             G < 1 for a grouped call, unknown tile
                             or scale kind; N not a multiple of 256
                             for the fused calls */
@@ -72,7 +79,7 @@ enum { FG_SELECT_SWIGLU_QUANT = 0x100 };
 
 /*
  * Dense ("normal") layout. zwzgs.cn DeepGEMM page, "Features > layouts".
- *   A  [M][K] E4M3, sa [K/128][M] fp32, B [N][K] E4M3, sb [N/128][K/128] fp32,
+ *   A  [M][K] E4M3, sa [K/128][M] fp32, B [N][K] E4M3, sb [ceil(N/128)][K/128] fp32,
  *   D  [M][N] bf16 (written in full).
  * M == 0 (or N == 0) returns FG_OK without launching anything.
  */
@@ -84,7 +91,7 @@ int fg_gemm_fp8_nt(const void* A, const float* sa, const void* B, const float* s
  * page, "Features > layouts" and "Applications > MoE".
  *   A  [M][K] E4M3: the rows of all G experts concatenated along M,
  *   sa [K/128][M], B [G][N][K] E4M3 (one weight per expert),
- *   sb [G][N/128][K/128], D [M][N] bf16,
+ *   sb [G][ceil(N/128)][K/128], D [M][N] bf16,
  *   m_indices [M] int32 (device): expert id of each row, or -1 for a padding
  *   row. Every aligned 128-row block of A must hold rows of at most one expert
  *   (plus padding rows); experts' segments are therefore padded to multiples
@@ -99,7 +106,7 @@ int fg_grouped_contiguous(const void* A, const float* sa, const void* B, const f
  * MoE grouped, masked layout (decode). zwzgs.cn DeepGEMM page, "Features >
  * layouts" and "Applications > MoE".
  *   A  [G][M_max][K] E4M3, sa [G][K/128][M_max], B [G][N][K] E4M3,
- *   sb [G][N/128][K/128], D [G][M_max][N] bf16,
+ *   sb [G][ceil(N/128)][K/128], D [G][M_max][N] bf16,
  *   masked_m [G] int32 (device): number of valid rows of each expert, clamped
  *   to [0, M_max] by the kernel. Only rows r < masked_m[g] of expert g are
  *   written; the rest of D keeps its prior content. masked_m is read only by
@@ -215,7 +222,9 @@ int fg_quant_act_1x128(const float* x, void* q, float* sa, int batch, int M, int
 
 /* Weights, 128x128 blocks: w [rows][K] fp32 with rows % 128 == 0 (a grouped
  *   weight [G][N][K] is rows = G*N), q [rows][K] E4M3, sb [rows/128][K/128]
- *   fp32 (= [G][N/128][K/128]). */
+ *   fp32 (= [G][N/128][K/128]). Weights with N not a multiple of 128 are
+ *   quantised by the caller (the last row block's scale from its N mod 128
+ *   rows). */
 int fg_quant_weight_128x128(const float* w, void* q, float* sb, int rows, int K,
                             hipStream_t stream);
 

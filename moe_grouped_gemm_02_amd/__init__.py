@@ -13,7 +13,7 @@ Tensor conventions (all on the same CUDA/HIP device, contiguous):
     A   uint8 or float8_e4m3fn  [M, K]        (masked: [G, M_max, K])
     sa  float32                 [K/128, M]    (masked: [G, K/128, M_max])
     B   uint8 or float8_e4m3fn  [N, K]        (grouped: [G, N, K])
-    sb  float32                 [N/128, K/128] (grouped: [G, N/128, K/128])
+    sb  float32                 [ceil(N/128), K/128] (grouped: [G, ceil(N/128), K/128])
     D   bfloat16                [M, N]        (masked: [G, M_max, N])
 """
 import ctypes
@@ -129,10 +129,10 @@ def _dense(fn, A, sa, B, sb, D):
     N = B.shape[0]
     _fp8(A, "A", (M, K))
     _fp8(B, "B", (N, K))
-    if K % 128 or N % 128:
-        raise ValueError("K and N must be multiples of 128")
+    if K % 128 or N % 8:
+        raise ValueError("K must be a multiple of 128 and N of 8")
     _dev(sa, "sa", (K // 128, M), torch.float32)
-    _dev(sb, "sb", (N // 128, K // 128), torch.float32)
+    _dev(sb, "sb", (-(-N // 128), K // 128), torch.float32)
     _dev(D, "D", (M, N), torch.bfloat16)
     _check(getattr(lib(), fn)(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D), M, N, K,
                               _stream(A)), fn)
@@ -156,10 +156,10 @@ def _contiguous(fn, A, sa, B, sb, D, m_indices):
     G, N = B.shape[0], B.shape[1]
     _fp8(A, "A", (M, K))
     _fp8(B, "B", (G, N, K))
-    if K % 128 or N % 128:
-        raise ValueError("K and N must be multiples of 128")
+    if K % 128 or N % 8:
+        raise ValueError("K must be a multiple of 128 and N of 8")
     _dev(sa, "sa", (K // 128, M), torch.float32)
-    _dev(sb, "sb", (G, N // 128, K // 128), torch.float32)
+    _dev(sb, "sb", (G, -(-N // 128), K // 128), torch.float32)
     _dev(D, "D", (M, N), torch.bfloat16)
     _dev(m_indices, "m_indices", (M,), torch.int32)
     _check(getattr(lib(), fn)(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D),
@@ -184,10 +184,10 @@ def _masked(fn, A, sa, B, sb, D, masked_m):
     N = B.shape[1]
     _fp8(A, "A", (G, M_max, K))
     _fp8(B, "B", (G, N, K))
-    if K % 128 or N % 128:
-        raise ValueError("K and N must be multiples of 128")
+    if K % 128 or N % 8:
+        raise ValueError("K must be a multiple of 128 and N of 8")
     _dev(sa, "sa", (G, K // 128, M_max), torch.float32)
-    _dev(sb, "sb", (G, N // 128, K // 128), torch.float32)
+    _dev(sb, "sb", (G, -(-N // 128), K // 128), torch.float32)
     _dev(D, "D", (G, M_max, N), torch.bfloat16)
     _dev(masked_m, "masked_m", (G,), torch.int32)
     _check(getattr(lib(), fn)(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D),

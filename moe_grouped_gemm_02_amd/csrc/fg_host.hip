@@ -157,7 +157,8 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 int run(int layout, const void* A, const float* sa, const void* B, const float* sb, void* D,
         const int32_t* m_indices, const int32_t* masked_m, int M, int N, int K, int G,
         hipStream_t stream, bool pow2, const FusedOut* fused = nullptr) {
-  if (M < 0 || N < 0 || K < 128 || (K % 128) != 0 || (N % 128) != 0) return FG_EINVAL;
+  // N: whole 16-byte pieces of bf16 output rows; K: whole 128-wide K-blocks
+  if (M < 0 || N < 0 || K < 128 || (K % 128) != 0 || (N % 8) != 0) return FG_EINVAL;
   if (fused && (N % 256) != 0) return FG_EINVAL;
   if (layout != FG_LAYOUT_DENSE && G < 1) return FG_EINVAL;
   if (M == 0 || N == 0) return FG_OK;
@@ -327,7 +328,7 @@ int fg_force_tile(int bm, int bn) {
 const char* fg_strerror(int code) {
   switch (code) {
     case FG_OK: return "success";
-    case FG_EINVAL: return "invalid argument (null pointer, negative size, K or N not a multiple of 128 (256 for the fused epilogue), K < 128, misaligned pointer, G < 1, unknown scale kind or tile)";
+    case FG_EINVAL: return "invalid argument (null pointer, negative size, K not a multiple of 128, N not a multiple of 8 (256 for the fused epilogue), K < 128, misaligned pointer, G < 1, unknown scale kind or tile)";
     case FG_EUNSUPPORTED: return "unsupported device (gfx950 required)";
     case FG_ELAUNCH: return "kernel launch failed";
     case FG_EDEVICE: return "HIP device query failed";

@@ -527,7 +527,8 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   const uint8_t* Ag = p.A + (LAYOUT == kMasked ? (size_t)g * M * K : 0);
   const float* sag = p.sa + (LAYOUT == kMasked ? (size_t)g * KB * M : 0);
   const uint8_t* Bg = p.B + (LAYOUT != kDense ? (size_t)g * p.N * K : 0);
-  const float* sbg = p.sb + (LAYOUT != kDense ? (size_t)g * (p.N / 128) * KB : 0);
+  const int NB128 = (p.N + 127) / 128;   // weight-scale row blocks (the last may be partial)
+  const float* sbg = p.sb + (LAYOUT != kDense ? (size_t)g * NB128 * KB : 0);
   uint16_t* Dg = p.D + (LAYOUT == kMasked ? (size_t)g * M * p.N : 0);
 
   const i32x4 rsA = buffer_rsrc(Ag, (uint32_t)M * (uint32_t)K);
@@ -564,7 +565,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   // (i == BM/64, clamped); a wave without a load of its own repeats load 0.
   const int nb_tile = n0 >> 7;
   const i32x4 rsSA = buffer_rsrc(sag, (uint32_t)KB * (uint32_t)M * 4u);
-  const i32x4 rsSB = buffer_rsrc(sbg, (uint32_t)(p.N / 128) * (uint32_t)KB * 4u);
+  const i32x4 rsSB = buffer_rsrc(sbg, (uint32_t)NB128 * (uint32_t)KB * 4u);
   i32x4 rsS[T::SC_INSTR];
   uint32_t sc_off[T::SC_INSTR], sc_stride[T::SC_INSTR], sc_dst[T::SC_INSTR];
 #pragma unroll
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
     sc_dst[q] = lds_addr + T::SC_BASE + (is_b ? BM * 4 : i * 256);
     // weight scales: a tile reads at most the blocks nb_tile .. nb_tile+2, so
     // lanes past 3 repeat lane 3's row (one cache line instead of one per lane)
-    sc_off[q] = is_b ? (uint32_t)min(nb_tile + min(lane, 3), p.N / 128 - 1) * (uint32_t)KB * 4u
+    sc_off[q] = is_b ? (uint32_t)min(nb_tile + min(lane, 3), NB128 - 1) * (uint32_t)KB * 4u
                      : (uint32_t)min(m0 + i * 64 + lane, M - 1) * 4u;
   }
   const uint32_t wave_at = lds_addr + wave * 1024;   // this wave's 1 KB DMA slot in a tile region
@@ -613,8 +614,8 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
 
   // ---- scale blocks of B covered by this wave's columns (at most two)
   const int wn0 = n0 + wn * WN;
-  const int nb_lo = uniform(min(wn0 >> 7, p.N / 128 - 1));
-  const int nb_hi = uniform(min(nb_lo + 1, p.N / 128 - 1));
+  const int nb_lo = uniform(min(wn0 >> 7, NB128 - 1));
+  const int nb_hi = uniform(min(nb_lo + 1, NB128 - 1));
   // first sub-tile column whose scale block is nb_hi
   const int j_switch = T::STRADDLE ? uniform(((nb_lo + 1) * 128 - wn0) >> 4) : TN;
 

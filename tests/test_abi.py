@@ -49,7 +49,7 @@ GOOD = ctypes.c_void_p(0x100000)   # aligned, never dereferenced (validation fai
 
 @pytest.mark.parametrize("args", [
     (GOOD, GOOD, GOOD, GOOD, GOOD, 64, 256, 100, None),       # K not a multiple of 128
-    (GOOD, GOOD, GOOD, GOOD, GOOD, 64, 200, 256, None),       # N not a multiple of 128
+    (GOOD, GOOD, GOOD, GOOD, GOOD, 64, 196, 256, None),       # N not a multiple of 8
     (GOOD, GOOD, GOOD, GOOD, GOOD, -1, 256, 256, None),       # negative M
     (GOOD, GOOD, GOOD, GOOD, GOOD, 64, 256, 0, None),         # K < 128
     (None, GOOD, GOOD, GOOD, GOOD, 64, 256, 256, None),       # null A

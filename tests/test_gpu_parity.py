@@ -220,3 +220,44 @@ def test_every_loop_exit_phase(forced_tile, kblocks):
     out = run_dense(A, sa, B, sb)
     r = oracle.check(out, oracle.ref_dense(A, sa, B, sb))
     assert r["ok"], r
+
+
+# ---------------------------------------------------------------- N not a multiple of 128
+
+@pytest.mark.parametrize("forced_tile", TILES, indirect=True, ids=lambda t: f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("N", [8, 72, 200, 328])
+@pytest.mark.parametrize("pow2", [False, True], ids=["fp32_scales", "pow2_scales"])
+def test_every_tile_ragged_n(forced_tile, N, pow2):
+    """N a multiple of 8 only: the last weight-scale block covers N mod 128
+    rows, the last column tile is partial, columns >= N are never stored."""
+    print(f"tile {forced_tile} dense ragged N={N} pow2={pow2}", flush=True)
+    A, sa, B, sb = make_dense(150, N, 384, 500 + N, pow2=pow2)
+    assert sb.shape[0] == -(-N // 128)
+    Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
+    D = new_out((150, N))
+    (fg.gemm_fp8_nt_pow2 if pow2 else fg.gemm_fp8_nt)(Ad, sad, Bd, sbd, D)
+    torch.cuda.synchronize()
+    r = oracle.check(d_bits(D), oracle.ref_dense(A, sa, B, sb))
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("pow2", [False, True], ids=["fp32_scales", "pow2_scales"])
+def test_grouped_ragged_n(pow2):
+    print(f"grouped ragged N pow2={pow2}", flush=True)
+    A, sa, B, sb, mi = make_contiguous(3, 200, 384, 512, pow2=pow2, m_lo=1, m_hi=300)
+    Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
+    D = new_out((A.shape[0], 200))
+    (fg.grouped_contiguous_pow2 if pow2 else fg.grouped_contiguous)(Ad, sad, Bd, sbd, D, to_dev(mi))
+    torch.cuda.synchronize()
+    ref, valid = oracle.ref_contiguous(A, sa, B, sb, mi)
+    r = oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
+    assert r["ok"], r
+    A, sa, B, sb, _ = make_masked(3, 150, 328, 256, 513, pow2=pow2)
+    mm = np.array([150, 0, 61], np.int32)
+    Ad, sad, Bd, sbd = masked_inputs(A, sa, B, sb)
+    D = new_out((3, 150, 328))
+    (fg.grouped_masked_pow2 if pow2 else fg.grouped_masked)(Ad, sad, Bd, sbd, D, to_dev(mm))
+    torch.cuda.synchronize()
+    ref, valid = oracle.ref_masked(A, sa, B, sb, mm)
+    r = oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
+    assert r["ok"], r
