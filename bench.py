@@ -41,7 +41,7 @@ if ROOT not in sys.path:
 PEAK_FP8_TFLOPS = 256 * 2.4e9 * 8192 / 1e12    # 5033: 256 CUs x 2.4 GHz x 8192 FLOP/clk/CU
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_02_amd", "csrc", f)
-                  for f in ("fg_kernel.hpp", "fg_e4m3.hpp", "fg_host.hip")]
+                  for f in ("fg_kernel.hpp", "fg_e4m3.hpp", "fg_tiles.hpp", "fg_launch.hip", "fg_host.hip")]
 PEAK_HBM_GBPS = 8000.0                          # HBM3E, 8 TB/s
 MALL_BYTES = 256 << 20
 HEADLINE = "dense_skinny"

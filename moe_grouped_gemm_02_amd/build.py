@@ -2,7 +2,9 @@
 
 Run ``python -m moe_grouped_gemm_02_amd.build`` (or call ``build()``). The
 shared object is written next to this file so that it travels with the source
-tree; nothing is installed elsewhere.
+tree; nothing is installed elsewhere. The GEMM kernels of each layout and scale
+kind are compiled as separate objects (fg_launch.hip with FG_LAUNCH_PART =
+2 * layout + pow2), in parallel, then linked with the host and quantiser code.
 """
 import os
 import subprocess
@@ -11,9 +13,13 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfg.so")
-SOURCES = ["fg_host.hip", "fg_quant.hip"]
-HEADERS = ["fg_kernel.hpp", "fg_e4m3.hpp"]
+LAUNCH_PARTS = 6   # {dense, contiguous, masked} x {fp32 scales, power-of-two scales}
+# (object name, source, extra flags)
+UNITS = [("fg_host", "fg_host.hip", []), ("fg_quant", "fg_quant.hip", [])] + [
+    (f"fg_launch_{i}", "fg_launch.hip", [f"-DFG_LAUNCH_PART={i}"]) for i in range(LAUNCH_PARTS)]
+HEADERS = ["fg_kernel.hpp", "fg_e4m3.hpp", "fg_tiles.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -21,7 +27,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 VALU forms stay off: plain v_fma_f32 only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA results straight into VGPRs: the promotion FMA reads them there
@@ -31,15 +36,38 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", LIB + ".tmp"]
+def build(verbose=False, jobs=None):
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = jobs or min(len(UNITS), max(1, len(os.sched_getaffinity(0))), 16)
+    pending = list(UNITS)
+    running = []
+    objs = []
+    failed = []
+    while pending or running:
+        while pending and len(running) < jobs:
+            name, src, extra = pending.pop(0)
+            obj = os.path.join(OBJ, name + ".o")
+            cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
+                   os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            running.append((name, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                                   text=True)))
+            objs.append(obj)
+        name, proc = running.pop(0)
+        out, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(name)
+    if failed:
+        raise RuntimeError("hipcc failed building " + ", ".join(failed))
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libfg.so")
+        raise RuntimeError("hipcc failed linking libfg.so")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -8,7 +8,7 @@
 #include <cstring>
 
 #include "fg.h"
-#include "fg_kernel.hpp"
+#include "fg_tiles.hpp"
 
 namespace {
 
@@ -43,16 +43,9 @@ struct Tile {
   int bm, bn, waves;
   double eff;   // fraction of the matrix-core rate the tile's K loop sustains
 };
-// Compiled tile shapes (rows x cols of D per workgroup), in the order of the
-// launch switch below.
-using Cfg0 = fg::TileCfg<256, 256, 4, 2, 2, false, 2, false, 3>;   // large dense / grouped
-using Cfg1 = fg::TileCfg<256, 128, 4, 2, 3, false, 2, false, 3>;
-using Cfg2 = fg::TileCfg<128, 256, 2, 4, 3, false, 2, false, 3>;   // contiguous (BM | 128)
-using Cfg3 = fg::TileCfg<128, 128, 2, 2, 4, false, 3, false, 3>;
-using Cfg4 = fg::TileCfg<64, 112, 4, 1, 6, true, 6, true, 3, 3>;     // skinny M, HBM-bound
-using Cfg5 = fg::TileCfg<256, 112, 4, 1, 3, true, 2, false, 3>;    // masked decode, HBM-bound
-using Cfg6 = fg::TileCfg<256, 224, 4, 2, 2, true, 2, false, 3>;    // N = 7168: 32 column tiles
-constexpr Tile kTiles[] = {{256, 256, Cfg0::W, 0.70}, {256, 128, Cfg1::W, 0.75},
+// The compiled tile shapes (fg_tiles.hpp), in the order of its launch switch.
+using namespace fg::tiles;
+constexpr Tile kTiles[] = {{256, 256, Cfg0::W, 0.75}, {256, 128, Cfg1::W, 0.75},
                            {128, 256, Cfg2::W, 0.75}, {128, 128, Cfg3::W, 0.70},
                            {64, 112, Cfg4::W, 0.60},  {256, 112, Cfg5::W, 0.70},
                            {256, 224, Cfg6::W, 0.70}};
@@ -63,11 +56,39 @@ std::atomic<int> g_forced_tile{-1};
 
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
-// Number of tiles a problem splits into with a given tile shape.
+// Contiguous layout: tiles of at most 128 rows sit on the aligned 128-row
+// expert blocks; 256-row tiles follow each expert's run of blocks, from a tile
+// list the kernel derives from m_indices (at most kRunMaxBlocks blocks).
+bool run_path(int layout, const Tile& t) { return layout == FG_LAYOUT_CONTIGUOUS && t.bm == 256; }
+bool tile_allowed(int layout, int M, int G, const Tile& t) {
+  if (layout != FG_LAYOUT_CONTIGUOUS || 128 % t.bm == 0) return true;
+  return run_path(layout, t) && ceil_div(M, 128) <= fg::kRunMaxBlocks && G <= fg::kRunMaxExperts;
+}
+// 256-row contiguous tiles per column: a run of r blocks takes ceil(r/2), so
+// with at most G runs (one per expert) there are at most ceil((blocks+G)/2);
+// the cost model takes half of the runs as odd.
+long run_tiles_m(int M, int G, bool bound) {
+  const long nblk = ceil_div(M, 128);
+  const long m = bound ? (nblk + G + 1) / 2 : (2 * nblk + G + 3) / 4;
+  return m < nblk ? m : nblk;
+}
+
+// Number of tiles a problem splits into with a given tile shape (the
+// contiguous 256-row case: the cost model's estimate).
 long count_tiles(int layout, int M, int N, int G, const Tile& t) {
   const long tn = ceil_div(N, t.bn);
   if (layout == FG_LAYOUT_MASKED) return (long)G * ceil_div(M, t.bm) * tn;
+  if (run_path(layout, t)) return run_tiles_m(M, G, false) * tn;
   return (long)ceil_div(M, t.bm) * tn;
+}
+
+// Workgroups a launch uses: one per tile, except the contiguous 256-row case,
+// whose workgroups walk the tile list persistently (at most one per CU, as
+// many as the largest possible list needs).
+long launch_grid(int layout, int M, int N, int G, const Tile& t, int cus) {
+  if (!run_path(layout, t)) return count_tiles(layout, M, N, G, t);
+  const long most = run_tiles_m(M, G, true) * ceil_div(N, t.bn);
+  return most < cus ? most : cus;
 }
 
 // Picks the tile for a problem: the compiled shape with the smallest
@@ -92,7 +113,7 @@ int pick_tile(int layout, int M, int N, int K, int G, int cus, bool bn256 = fals
   const double kblocks = K / 128;
   for (int i = 0; i < kNumTiles; ++i) {
     const Tile& t = kTiles[i];
-    if (layout == FG_LAYOUT_CONTIGUOUS && 128 % t.bm != 0) continue;
+    if (!tile_allowed(layout, M, G, t)) continue;
     if (bn256 && t.bn != 256) continue;
     const long tiles = count_tiles(layout, M, N, G, t);
     const long rounds = (tiles + cus - 1) / cus;
@@ -107,37 +128,12 @@ int pick_tile(int layout, int M, int N, int K, int G, int cus, bool bn256 = fals
   return best;
 }
 
-// One tile configuration; the fused epilogue exists only for 256-column tiles.
-template <int LAYOUT, bool POW2, int EPI, class C>
-hipError_t launch_tile(const Params& p, int grid, hipStream_t s) {
-  if constexpr (EPI == fg::kEpiSwigluQuant && C::BN != 256) {
-    return hipErrorInvalidValue;
-  } else {
-    hipLaunchKernelGGL((fg::fp8_bs_gemm<LAYOUT, C, POW2, EPI>), dim3(grid), dim3(C::THREADS), 0, s, p);
-    return hipGetLastError();
-  }
-}
-
-template <int LAYOUT, bool POW2, int EPI>
-hipError_t launch_layout(int tile, const Params& p, int grid, hipStream_t s) {
-  switch (tile) {
-    case 0: return launch_tile<LAYOUT, POW2, EPI, Cfg0>(p, grid, s);
-    case 1: return launch_tile<LAYOUT, POW2, EPI, Cfg1>(p, grid, s);
-    case 2: return launch_tile<LAYOUT, POW2, EPI, Cfg2>(p, grid, s);
-    case 3: return launch_tile<LAYOUT, POW2, EPI, Cfg3>(p, grid, s);
-    case 4: return launch_tile<LAYOUT, POW2, EPI, Cfg4>(p, grid, s);
-    case 5: return launch_tile<LAYOUT, POW2, EPI, Cfg5>(p, grid, s);
-    case 6: return launch_tile<LAYOUT, POW2, EPI, Cfg6>(p, grid, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 template <bool POW2, int EPI>
 hipError_t launch(int layout, int tile, const Params& p, int grid, hipStream_t s) {
   switch (layout) {
-    case FG_LAYOUT_DENSE: return launch_layout<fg::kDense, POW2, EPI>(tile, p, grid, s);
-    case FG_LAYOUT_CONTIGUOUS: return launch_layout<fg::kContiguous, POW2, EPI>(tile, p, grid, s);
-    default: return launch_layout<fg::kMasked, POW2, EPI>(tile, p, grid, s);
+    case FG_LAYOUT_DENSE: return fg::launch_layout<fg::kDense, POW2, EPI>(tile, p, grid, s);
+    case FG_LAYOUT_CONTIGUOUS: return fg::launch_layout<fg::kContiguous, POW2, EPI>(tile, p, grid, s);
+    default: return fg::launch_layout<fg::kMasked, POW2, EPI>(tile, p, grid, s);
   }
 }
 
@@ -184,8 +180,8 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   const int ti = pick_tile(layout, M, N, K, G, cus, fused != nullptr);
   if (ti < 0) return FG_EINVAL;   // a forced tile the fused epilogue cannot use
   const Tile& t = kTiles[ti];
-  // contiguous tiles must not straddle an aligned 128-row expert block
-  if (layout == FG_LAYOUT_CONTIGUOUS && 128 % t.bm != 0) return FG_EINVAL;
+  // a forced tile the contiguous layout cannot use at this size
+  if (!tile_allowed(layout, M, G, t)) return FG_EINVAL;
   Params p;
   p.A = static_cast<const uint8_t*>(A);
   p.sa = sa;
@@ -202,9 +198,9 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   p.K = K;
   p.G = layout == FG_LAYOUT_DENSE ? 1 : G;
   p.KB = K / 128;
-  p.tiles_m = ceil_div(M, t.bm);
+  p.tiles_m = ceil_div(M, t.bm);   // the contiguous 256-row kernel counts its own
   p.tiles_n = ceil_div(N, t.bn);
-  const long tiles = count_tiles(layout, M, N, p.G, t);
+  const long tiles = launch_grid(layout, M, N, p.G, t, cus);
   if (tiles > 0x7fffffffL) return FG_EINVAL;
   const int grid = (int)tiles;
 
@@ -307,7 +303,7 @@ int fg_select_config(int layout, int M, int N, int K, int G, int num_cus, int* b
   if (ti < 0) return FG_EINVAL;
   if (bm) *bm = kTiles[ti].bm;
   if (bn) *bn = kTiles[ti].bn;
-  if (grid) *grid = (int)count_tiles(layout, M, N, G, kTiles[ti]);
+  if (grid) *grid = (int)launch_grid(layout, M, N, G, kTiles[ti], cus);
   return FG_OK;
 }
 

@@ -91,6 +91,9 @@ enum Epilogue { kEpiBf16 = 0, kEpiSwigluQuant = 1 };
 constexpr int kKBlock = 128;   // scale block along K (elements == bytes)
 constexpr int kXCDs = 8;       // MI355X: workgroups go round-robin to 8 XCDs
 constexpr int kGroupM = 4;     // m-blocks per rasterisation group
+// A DMA lane offset past every operand's buffer (the host keeps one expert's
+// A and B below 2^31 bytes): the buffer range check turns the load into zeros.
+constexpr uint32_t kNoRow = 0x80000000u;
 
 struct Params {
   const uint8_t* A;       // E4M3 [rows][K] (masked: [G][M][K])
@@ -455,15 +458,14 @@ __device__ __forceinline__ void swiglu_quant_epilogue(const Params& p, const f32
   }
 }
 
-template <int LAYOUT, class T, bool POW2 = false, int EPI = kEpiBf16>
-__global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
+// One BM x BN output tile of expert g (dense: g = 0) whose first row is m0
+// and first column n0; rows_valid bounds the rows that have an output.
+template <int LAYOUT, class T, bool POW2, int EPI>
+__device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, int g, const int m0,
+                                          const int n0, const int rows_valid) {
   constexpr int BM = T::BM, BN = T::BN, W = T::W, WM = T::WM, WN = T::WN;
   constexpr int TM = T::TM, TN = T::TN, PD = T::PD, R = T::RING;
   constexpr int PL = T::PL, P = T::PARTS;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
-  __shared__ int s_group;
-  lds_u8* const lds = (lds_u8*)smem;
-
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = uniform(t >> 6);
@@ -473,54 +475,6 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   const int wm = EPI == kEpiSwigluQuant ? wave % T::WGM : wave / T::WGN;
   const int wn = EPI == kEpiSwigluQuant ? wave / T::WGM : wave % T::WGN;
   const int lr = lane & 15, lq = lane >> 4;
-
-  // ---- workgroup -> tile. Consecutive tile ids are placed on the same XCD
-  // (workgroups are dealt round-robin to the XCDs), then tiles are walked in
-  // groups of kGroupM m-blocks so the tiles resident on one XCD share A rows
-  // and B columns in its L2.
-  int tile;
-  {
-    const int b = blockIdx.x, nwg = gridDim.x;
-    const int x = b % kXCDs, l = b / kXCDs;
-    const int per = nwg / kXCDs, rem = nwg % kXCDs;
-    tile = x * per + (x < rem ? x : rem) + l;
-  }
-  int g = 0;
-  if (LAYOUT == kMasked) {
-    const int per = p.tiles_m * p.tiles_n;
-    g = tile / per;
-    tile -= g * per;
-  }
-  int mb, nbk;
-  {
-    const int span = kGroupM * p.tiles_n;
-    const int grp = tile / span;
-    const int first = grp * kGroupM;
-    const int gsz = min(kGroupM, p.tiles_m - first);
-    const int in = tile - grp * span;
-    mb = first + in % gsz;
-    nbk = in / gsz;
-  }
-  const int m0 = mb * BM, n0 = nbk * BN;
-
-  int rows_valid = p.M;  // rows of this slab that have an output
-  if (LAYOUT == kMasked) {
-    int mm = p.masked_m[g];
-    mm = mm < 0 ? 0 : (mm > p.M ? p.M : mm);
-    if (m0 >= mm) return;  // uniform over the workgroup
-    rows_valid = mm;
-  }
-  if (LAYOUT == kContiguous) {
-    if (t == 0) s_group = -1;
-    __syncthreads();
-    if (t < BM && m0 + t < p.M) {
-      const int id = p.m_indices[m0 + t];
-      if (id >= 0 && id < p.G) atomicMax(&s_group, id);
-    }
-    __syncthreads();
-    g = s_group;
-    if (g < 0) return;  // all-padding block
-  }
   g = uniform(g);
 
   const int K = p.K, KB = p.KB, M = p.M;
@@ -543,22 +497,28 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   // ---- DMA sources: a buffer resource per operand and per-lane byte offsets
   // within one K-block column. Slot s of a tile region is the 16-byte LDS
   // chunk s; it holds row s/8, chunk position s%8, i.e. global chunk
-  // (s%8) ^ (row%8). Rows past the tile (padding slots) and past the matrix
-  // are clamped to a valid row.
+  // (s%8) ^ (row%8). Rows that have no output -- padding slots past the tile,
+  // A rows past M, masked rows at or beyond masked_m[g], contiguous rows of
+  // padding or of another expert, B rows past N -- get the offset kNoRow,
+  // beyond the operand's buffer: the range check returns zeros for them
+  // without a memory access, so they cost no traffic and their MFMAs multiply
+  // zeros (the matrix core draws less power on them).
   uint32_t a_off[T::A_INSTR], b_off[T::B_INSTR];
 #pragma unroll
   for (int q = 0; q < T::A_INSTR; ++q) {
     const int slot = (q * W + wave) * 64 + lane;
     const int row = slot >> 3, chunk = (slot & 7) ^ (row & 7);
-    const int m = min(m0 + min(row, BM - 1), M - 1);
-    a_off[q] = (uint32_t)m * (uint32_t)K + chunk * 16;
+    const int m = m0 + row;
+    bool live = row < BM && m < rows_valid;
+    if (LAYOUT == kContiguous && live) live = p.m_indices[m] == g;
+    a_off[q] = live ? (uint32_t)m * (uint32_t)K + chunk * 16 : kNoRow;
   }
 #pragma unroll
   for (int q = 0; q < T::B_INSTR; ++q) {
     const int slot = (q * W + wave) * 64 + lane;
     const int row = slot >> 3, chunk = (slot & 7) ^ (row & 7);
-    const int n = min(n0 + min(row, BN - 1), p.N - 1);
-    b_off[q] = (uint32_t)n * (uint32_t)K + chunk * 16;
+    const int n = n0 + row;
+    b_off[q] = row < BN && n < p.N ? (uint32_t)n * (uint32_t)K + chunk * 16 : kNoRow;
   }
   // Scale loads: load i = q*W + wave brings activation rows [64i, 64i+64)
   // (i < BM/64) or the weight scales of the tile's 128-column blocks
@@ -930,5 +890,159 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
     }
   }
 }
+
+// Contiguous layout with 256-row tiles. Experts' row segments are padded only
+// to 128 rows, so 256-row tiles on a fixed 256-row grid would straddle two
+// experts wherever a segment starts at an odd 128-row block. A tile instead
+// starts at the first 128-row block of each run of blocks that belong to one
+// expert, and at every second block after it. The last tile of a run with an
+// odd number of blocks covers one block of the run; its other 128 rows
+// (another expert's, padding, or past M) are computed with this expert's
+// weight and never stored, since rows are stored only where m_indices names
+// the tile's expert. The runs depend on m_indices, which lives in device
+// memory, so every workgroup derives the tile list itself and the workgroups
+// walk it persistently (a fixed grid; tile i goes to workgroup i mod grid).
+constexpr int kRunMaxBlocks = 2048;    // 128-row blocks one list holds (M <= 262144)
+constexpr int kRunMaxExperts = 32767;  // experts a packed list entry can name
+template <int LAYOUT, class T>
+constexpr bool run_tiles() {
+  return LAYOUT == kContiguous && T::BM == 256;
+}
+
+// The tile list of the 256-row contiguous layout. Pass 1 (all threads, 32
+// lanes per block): the expert of each 128-row block -- the largest valid id
+// among its rows, -1 if it has none, the rule the 128-row tiles use -- into
+// blk[]. Pass 2 (wave 0, 64 blocks at a time, one lane each): a block starts
+// a run when its expert differs from the previous block's, and starts a tile
+// when it lies an even number of blocks after its run's start. Entry i of
+// list[] is (block | expert << 16) of the i-th tile in row order. Returns the
+// number of tiles; every thread of the workgroup must call it.
+template <int THREADS>
+__device__ __forceinline__ int contiguous_run_tiles(const Params& p, int* blk, int* list, int* s_count) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int nblk = (p.M + 127) / 128;
+  constexpr int BPI = THREADS / 32;   // blocks per pass-1 iteration
+  const int iters = (nblk + BPI - 1) / BPI;
+  for (int it = 0; it < iters; ++it) {   // same trip count for every lane (shuffles below)
+    const int bk = it * BPI + (t >> 5), h = t & 31;
+    int v = -1;
+    if (bk < nblk) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = bk * 128 + r * 32 + h;
+        if (m < p.M) {
+          const int id = p.m_indices[m];
+          if (id >= 0 && id < p.G) v = max(v, id);
+        }
+      }
+    }
+#pragma unroll
+    for (int d = 16; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, 32));
+    if (h == 0 && bk < nblk) blk[bk] = v;
+  }
+  __syncthreads();
+  if (t < 64) {
+    int prev_e = -1, prev_rs = 0, count = 0;
+    const unsigned long long lt = (1ull << lane) - 1ull, le = lt | (1ull << lane);
+    for (int c0 = 0; c0 < nblk; c0 += 64) {
+      const int bk = c0 + lane;
+      const int e = bk < nblk ? blk[bk] : -1;
+      int before = __shfl_up(e, 1);
+      if (lane == 0) before = prev_e;
+      const unsigned long long starts = __ballot(e >= 0 && e != before) & le;
+      const int rs = starts ? c0 + 63 - __clzll((long long)starts) : prev_rs;   // start of this block's run
+      const bool first = e >= 0 && ((bk - rs) & 1) == 0;
+      const unsigned long long firsts = __ballot(first);
+      if (first) list[count + __popcll(firsts & lt)] = bk | (e << 16);
+      count += __popcll(firsts);
+      prev_e = __shfl(e, 63);
+      prev_rs = __shfl(rs, 63);
+    }
+    if (t == 0) *s_count = count;
+  }
+  __syncthreads();
+  return *s_count;
+}
+
+template <int LAYOUT, class T, bool POW2 = false, int EPI = kEpiBf16>
+__global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
+  constexpr int BM = T::BM, BN = T::BN;
+  constexpr bool RUNS = run_tiles<LAYOUT, T>();
+  constexpr int LIST_BYTES = RUNS ? kRunMaxBlocks * 4 : 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES + LIST_BYTES];
+  __shared__ int s_group;
+  lds_u8* const lds = (lds_u8*)smem;
+  const int t = threadIdx.x;
+
+  // ---- workgroup -> tile position. Consecutive positions are placed on the
+  // same XCD (workgroups are dealt round-robin to the XCDs); tiles are walked
+  // in groups of kGroupM m-blocks so the tiles resident on one XCD share A
+  // rows and B columns in its L2.
+  int pos;
+  {
+    const int b = blockIdx.x, nwg = gridDim.x;
+    const int x = b % kXCDs, l = b / kXCDs;
+    const int per = nwg / kXCDs, rem = nwg % kXCDs;
+    pos = x * per + (x < rem ? x : rem) + l;
+  }
+  auto raster = [&](int tile, int tiles_m, int& mb, int& nbk) {
+    const int span = kGroupM * p.tiles_n;
+    const int grp = tile / span;
+    const int first = grp * kGroupM;
+    const int gsz = min(kGroupM, tiles_m - first);
+    const int in = tile - grp * span;
+    mb = first + in % gsz;
+    nbk = in / gsz;
+  };
+
+  if constexpr (RUNS) {
+    int* list = (int*)(smem + T::LDS_BYTES);
+    const int ntm = contiguous_run_tiles<T::THREADS>(p, (int*)smem, list, &s_group);
+    const int total = ntm * p.tiles_n;
+    for (int tile = pos; tile < total; tile += gridDim.x) {
+      if (tile != pos) {   // the previous tile's epilogue is done with LDS
+        wait_vm<0>();
+        wait_lgkm0();
+        block_barrier();
+      }
+      int mb, nbk;
+      raster(tile, ntm, mb, nbk);
+      const int e = list[mb];
+      gemm_tile<LAYOUT, T, POW2, EPI>(p, lds, e >> 16, (e & 0xffff) * 128, nbk * BN, p.M);
+    }
+  } else {
+    int tile = pos;
+    int g = 0;
+    if (LAYOUT == kMasked) {
+      const int per = p.tiles_m * p.tiles_n;
+      g = tile / per;
+      tile -= g * per;
+    }
+    int mb, nbk;
+    raster(tile, p.tiles_m, mb, nbk);
+    const int m0 = mb * BM, n0 = nbk * BN;
+
+    int rows_valid = p.M;  // rows of this slab that have an output
+    if (LAYOUT == kMasked) {
+      int mm = p.masked_m[g];
+      mm = mm < 0 ? 0 : (mm > p.M ? p.M : mm);
+      if (m0 >= mm) return;  // uniform over the workgroup
+      rows_valid = mm;
+    }
+    if (LAYOUT == kContiguous) {
+      if (t == 0) s_group = -1;
+      __syncthreads();
+      if (t < BM && m0 + t < p.M) {
+        const int id = p.m_indices[m0 + t];
+        if (id >= 0 && id < p.G) atomicMax(&s_group, id);
+      }
+      __syncthreads();
+      g = s_group;
+      if (g < 0) return;  // all-padding block
+    }
+    gemm_tile<LAYOUT, T, POW2, EPI>(p, lds, g, m0, n0, rows_valid);
+  }
+}
+
 
 }  // namespace fg

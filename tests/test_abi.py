@@ -125,7 +125,7 @@ def test_fused_select_config_uses_256_column_tiles():
         bm, bn, grid = fg.select_config(layout | fg.SELECT_SWIGLU_QUANT, M, N, K, G)
         assert bn == 256
         if layout == 1:
-            assert 128 % bm == 0
+            assert 128 % bm == 0 or bm == 256
 
 
 def test_select_config_fills_the_machine():
@@ -135,9 +135,17 @@ def test_select_config_fills_the_machine():
         bm, bn, grid = fg.select_config(layout, M, N, K, G)
         assert bm > 0 and bn > 0 and N % 16 == 0
         tiles = -(-M // bm) * -(-N // bn) * (G if layout == 2 else 1)
-        assert grid == tiles
+        if layout == 1 and bm == 256:
+            # 256-row contiguous tiles follow the experts' runs of 128-row blocks;
+            # the workgroups walk the tile list persistently, one per CU at most,
+            # as many as the largest list needs (ceil((blocks + G) / 2) per column)
+            blocks = -(-M // 128)
+            most = min(blocks, (blocks + G + 1) // 2) * -(-N // bn)
+            assert grid == min(most, 256)
+        else:
+            assert grid == tiles
         if layout == 1:
-            assert 128 % bm == 0         # contiguous tiles never straddle an expert block
+            assert 128 % bm == 0 or bm == 256   # 128-row blocks, or the run-following 256-row tiles
 
 
 def test_select_config_picks_the_measured_best_tiles():
@@ -148,7 +156,7 @@ def test_select_config_picks_the_measured_best_tiles():
     # splits N = 7168 into 32 whole column tiles), and the widest tile with
     # BM | 128 for the contiguous layout.
     assert fg.select_config(0, 256, 7168, 7168, 1)[:2] == (64, 112)
-    assert fg.select_config(1, 9472, 4096, 7168, 8)[:2] == (128, 256)
+    assert fg.select_config(1, 9472, 4096, 7168, 8)[:2] == (256, 224)
     assert fg.select_config(2, 256, 7168, 2048, 16)[:2] in ((256, 224), (256, 256))
     assert fg.select_config(0, 8192, 7168, 18432, 1)[:2] in ((256, 128), (256, 256), (256, 224))
 

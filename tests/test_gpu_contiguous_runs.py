@@ -1,0 +1,94 @@
+"""GPU parity of the contiguous layout on 256-row tiles. Experts are padded
+only to 128 rows, so those tiles follow each expert's run of 128-row blocks
+from a tile list the kernel derives from m_indices: tiles start at a run's
+first block and every second block after it, and the workgroups walk the list
+persistently. These cases put run boundaries at odd blocks, across the 64-block
+steps of the device-side scan, around all-padding blocks and partial tails, and
+give an expert more than one run (more tiles than the launch has workgroups)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import moe_grouped_gemm_02_amd as fg
+from fgtest import SENTINEL, d_bits, dense_inputs, new_out, to_dev
+
+pytestmark = pytest.mark.gpu
+
+RUN_TILES = [(256, 224), (256, 128), (256, 256), (256, 112)]
+
+
+def m_indices_from(segments, tail_rows=0):
+    """segments: (expert, real rows, padded rows) in row order; expert -1 is a
+    block of padding. tail_rows: an extra partial block of expert -1 rows."""
+    ids = []
+    for e, real, padded in segments:
+        ids += [e] * real + [-1] * (padded - real)
+    ids += [-1] * tail_rows
+    return np.asarray(ids, np.int32)
+
+
+def run_case(mi, G, N, K, seed, tile):
+    rng = np.random.default_rng(seed)
+    M = mi.shape[0]
+    a = rng.standard_normal((M, K), dtype=np.float32)
+    b = rng.standard_normal((G, N, K), dtype=np.float32)
+    A, sa = oracle.quantize_act_1x128(a)
+    B, sb = oracle.quantize_weight_128x128(b)
+    Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
+    D = new_out((M, N))
+    fg.force_tile(*tile)
+    try:
+        fg.grouped_contiguous(Ad, sad, Bd, sbd, D, to_dev(mi))
+    finally:
+        fg.force_tile(0, 0)
+    torch.cuda.synchronize()
+    # ids outside [0, G) are padding: no output, not written
+    mi_ref = np.where((mi >= 0) & (mi < G), mi, -1)
+    ref, valid = oracle.ref_contiguous(A, sa, B, sb, mi_ref)
+    return oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
+
+
+CASES = {
+    # odd runs, a one-block run, an all-padding block between experts, a
+    # partial final block
+    "odd_runs": ([(2, 300, 384), (-1, 0, 128), (0, 100, 128), (1, 256, 256), (3, 129, 256)], 77, 4),
+    # one expert in several runs (5 tiles per column where 2 experts bound 3)
+    "split_expert": ([(0, 128, 128), (1, 128, 128), (0, 128, 128), (1, 50, 128), (0, 128, 128)], 0, 2),
+    # runs that cross the scan's 64-block steps at odd offsets (141 blocks)
+    "many_blocks": ([(1, 63 * 128, 63 * 128), (0, 3 * 128 - 5, 3 * 128), (2, 70 * 128, 70 * 128),
+                     (0, 4 * 128, 4 * 128)], 40, 3),
+}
+
+
+@pytest.mark.parametrize("tile", RUN_TILES, ids=lambda t: f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("case", list(CASES))
+def test_contiguous_run_tiles(case, tile):
+    segs, tail, G = CASES[case]
+    mi = m_indices_from(segs, tail)
+    N, K = (256, 256) if case == "many_blocks" else (384, 640)
+    print(f"contiguous runs {case} tile {tile} M={mi.shape[0]} N={N} K={K} G={G}", flush=True)
+    r = run_case(mi, G, N, K, 70 + len(mi), tile)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("tile", RUN_TILES[:1], ids=lambda t: f"{t[0]}x{t[1]}")
+def test_contiguous_run_tiles_ids_out_of_range(tile):
+    """Ids >= G count as padding: such rows are not written and do not decide a
+    block's expert."""
+    mi = m_indices_from([(0, 200, 256), (1, 128, 128)], 0)
+    mi[5] = 7
+    mi[130] = 99
+    mi[300] = 2
+    print(f"contiguous runs ids out of range tile {tile}", flush=True)
+    r = run_case(mi, 2, 384, 256, 91, tile)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("tile", RUN_TILES[:1], ids=lambda t: f"{t[0]}x{t[1]}")
+def test_contiguous_run_tiles_all_padding(tile):
+    """No row has an expert: nothing is written."""
+    mi = np.full(384, -1, np.int32)
+    print(f"contiguous runs all padding tile {tile}", flush=True)
+    r = run_case(mi, 2, 256, 256, 92, tile)
+    assert r["ok"], r

@@ -198,7 +198,7 @@ def test_loop_exit_phases_pow2(forced_tile, kblocks):
     assert r["ok"], r
 
 
-@pytest.mark.parametrize("forced_tile", [None] + [t for t in TILES if 128 % t[0] == 0], indirect=True,
+@pytest.mark.parametrize("forced_tile", [None] + TILES, indirect=True,
                          ids=lambda t: "auto" if t is None else f"{t[0]}x{t[1]}")
 def test_contiguous_pow2(forced_tile):
     print(f"pow2 contiguous tile {forced_tile}", flush=True)

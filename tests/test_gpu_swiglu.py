@@ -93,7 +93,7 @@ def test_dense_swiglu_quant(forced_tile, M, N, K, seed, pow2):
     check_rows(Q.cpu().numpy(), sq.cpu().numpy().T, act.cpu().numpy(), ref_act, np.ones(M, bool), pow2)
 
 
-@pytest.mark.parametrize("forced_tile", [None, (128, 256)], indirect=True,
+@pytest.mark.parametrize("forced_tile", [None, (128, 256), (256, 256)], indirect=True,
                          ids=lambda t: "auto" if t is None else f"{t[0]}x{t[1]}")
 @SCALES
 def test_contiguous_swiglu_quant(forced_tile, pow2):
