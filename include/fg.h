@@ -34,8 +34,9 @@
  *   - K must be a multiple of 128 and N a multiple of 8 (whole 16-byte pieces
  *     of a bf16 output row; the fused calls need N % 256 == 0); M is
  *     arbitrary (>= 0). The boundary handling the 2kiu.com explainer
- *     discusses in section 4.3 is done in one code path: loads past N are
- *     clamped to row N-1 and the stores of columns >= N are skipped.
+ *     discusses in section 4.3 is done in one code path: loads of rows past N
+ *     (and of A rows without an output) read zeros through the buffer range
+ *     check, and the stores of columns >= N are skipped.
  *   - A, B and D base pointers must be 16-byte aligned, sa and sb 4-byte.
  *   - Calls are asynchronous on `stream` (0 = null stream), never synchronise
  *     and never read device data on the host, so they can be captured in a
