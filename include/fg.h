@@ -202,7 +202,10 @@ int fg_select_config(int layout, int M, int N, int K, int G, int num_cus,
 
 /* Force a tile configuration for subsequent calls (bm x bn must be one of the
  * compiled tiles), or restore automatic selection with bm = bn = 0. Intended
- * for tests and tile sweeps; process-wide, not thread-safe. */
+ * for tests and tile sweeps; process-wide, not thread-safe. A call (and
+ * fg_select_config) returns FG_EINVAL if the forced tile does not suit it: a
+ * fused call needs 256 columns; a contiguous call takes 256-row tiles only
+ * while its device-side tile list fits (M <= 262144 rows, G <= 32767). */
 int fg_force_tile(int bm, int bn);
 
 /*

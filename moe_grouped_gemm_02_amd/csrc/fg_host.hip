@@ -107,7 +107,8 @@ long launch_grid(int layout, int M, int N, int G, const Tile& t, int cus) {
 constexpr double kTileFixedCycles = 4000.0;
 int pick_tile(int layout, int M, int N, int K, int G, int cus, bool bn256 = false) {
   const int forced = g_forced_tile.load(std::memory_order_relaxed);
-  if (forced >= 0) return (!bn256 || kTiles[forced].bn == 256) ? forced : -1;
+  if (forced >= 0)
+    return (!bn256 || kTiles[forced].bn == 256) && tile_allowed(layout, M, G, kTiles[forced]) ? forced : -1;
   int best = -1;
   double best_cost = 0.0;
   const double kblocks = K / 128;
@@ -178,10 +179,8 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   if (st != FG_OK) return st;
 
   const int ti = pick_tile(layout, M, N, K, G, cus, fused != nullptr);
-  if (ti < 0) return FG_EINVAL;   // a forced tile the fused epilogue cannot use
+  if (ti < 0) return FG_EINVAL;   // a forced tile this call cannot use
   const Tile& t = kTiles[ti];
-  // a forced tile the contiguous layout cannot use at this size
-  if (!tile_allowed(layout, M, G, t)) return FG_EINVAL;
   Params p;
   p.A = static_cast<const uint8_t*>(A);
   p.sa = sa;

@@ -172,3 +172,22 @@ def test_force_tile_roundtrip():
     fg.force_tile(0, 0)
     with pytest.raises(fg.FGError):
         fg.force_tile(96, 96)
+
+
+def test_contiguous_256_row_tiles_only_within_the_tile_list():
+    # The 256-row contiguous tiles follow a tile list each workgroup builds in
+    # LDS (at most 2048 blocks of 128 rows, experts < 32768); beyond that the
+    # choice falls back to tiles of at most 128 rows, and a forced 256-row tile
+    # is refused.
+    assert fg.select_config(1, 2048 * 128, 4096, 7168, 8)[0] == 256
+    assert fg.select_config(1, 2048 * 128 + 1, 4096, 7168, 8)[0] <= 128
+    assert fg.select_config(1, 9472, 4096, 7168, 32768)[0] <= 128
+    fg.force_tile(256, 224)
+    try:
+        assert fg.select_config(1, 9472, 4096, 7168, 8)[:2] == (256, 224)
+        with pytest.raises(fg.FGError):
+            fg.select_config(1, 2048 * 128 + 1, 4096, 7168, 8)
+        # dense and masked have no such limit
+        assert fg.select_config(0, 2048 * 128 + 1, 4096, 7168, 1)[:2] == (256, 224)
+    finally:
+        fg.force_tile(0, 0)
