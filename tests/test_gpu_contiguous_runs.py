@@ -55,6 +55,10 @@ CASES = {
     "odd_runs": ([(2, 300, 384), (-1, 0, 128), (0, 100, 128), (1, 256, 256), (3, 129, 256)], 77, 4),
     # one expert in several runs (5 tiles per column where 2 experts bound 3)
     "split_expert": ([(0, 128, 128), (1, 128, 128), (0, 128, 128), (1, 50, 128), (0, 128, 128)], 0, 2),
+    # fewer rows than one block
+    "tiny": ([(1, 5, 5)], 0, 2),
+    # one expert over an odd number of blocks (G = 1)
+    "one_expert": ([(0, 9 * 128 - 40, 9 * 128)], 0, 1),
     # runs that cross the scan's 64-block steps at odd offsets (141 blocks)
     "many_blocks": ([(1, 63 * 128, 63 * 128), (0, 3 * 128 - 5, 3 * 128), (2, 70 * 128, 70 * 128),
                      (0, 4 * 128, 4 * 128)], 40, 3),
