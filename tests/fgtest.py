@@ -1,6 +1,8 @@
 """Shared helpers for the GPU parity tests: seeded inputs quantised by the
 oracle on the CPU, marshalled into the library's layouts, and results brought
 back for the oracle's check. Nothing here computes the GEMM."""
+import functools
+
 import numpy as np
 import torch
 
@@ -91,3 +93,14 @@ def quant_inputs(shape, seed):
     mids = ((t[:-1] + t[1:]) / 2)
     flat[8, 1:127] = mids[:126]
     return x
+
+
+@functools.lru_cache(maxsize=2)
+def fullsize_contiguous(pow2=False):
+    """The contiguous MoE workload (8 experts, N 4096, K 7168) quantised by the
+    oracle: (A, sa, B, sb, m_indices), natural layouts; computed once per scale
+    kind and shared by the full-size tests (treat as read-only)."""
+    w = workloads.make("contiguous")
+    A, sa = oracle.quantize_act_1x128(w["a"], pow2)
+    B, sb = oracle.quantize_weight_128x128(w["b"], pow2)
+    return A, sa, B, sb, w["m_indices"]

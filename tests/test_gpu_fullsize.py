@@ -11,7 +11,7 @@ import torch
 import oracle
 import workloads
 import moe_grouped_gemm_02_amd as fg
-from fgtest import SENTINEL, d_bits, dense_inputs, masked_inputs, new_out, to_dev
+from fgtest import SENTINEL, d_bits, dense_inputs, fullsize_contiguous, masked_inputs, new_out, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -74,11 +74,7 @@ def test_fullsize_dense_ffn(pow2):
 @POW2
 def test_fullsize_contiguous(pow2):
     print(f"full contiguous 8 experts, N=4096, K=7168 pow2={pow2}", flush=True)
-    w = workloads.make("contiguous")
-    A, sa = oracle.quantize_act_1x128(w["a"], pow2)
-    B, sb = oracle.quantize_weight_128x128(w["b"], pow2)
-    mi = w["m_indices"]
-    del w
+    A, sa, B, sb, mi = fullsize_contiguous(pow2)
     Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
     M, N = A.shape[0], B.shape[1]
     D = new_out((M, N))

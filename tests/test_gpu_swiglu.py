@@ -23,7 +23,7 @@ import torch
 import oracle
 import workloads
 import moe_grouped_gemm_02_amd as fg
-from fgtest import make_contiguous, make_dense, make_masked, to_dev
+from fgtest import fullsize_contiguous, make_contiguous, make_dense, make_masked, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -195,4 +195,36 @@ def test_fullsize_masked_swiglu_quant(pow2):
         up = oracle.ref_entries(A[g], sa[g], B[g], sb[g], rows, gate_cols + 128)
         ref = oracle.silu(gate) * up
         r = check_f32(acth[g][rows, cols], ref)
+        assert r["ok"], (g, r)
+
+
+def test_fullsize_contiguous_swiglu_quant():
+    """The contiguous MoE workload (8 experts, 9472 rows with padding, N 4096 ->
+    I 2048, K 7168) on the automatically chosen tile (256x256, following the
+    experts' runs of 128-row blocks): codes and scales of every row with an
+    expert bit for bit against the oracle quantiser of the kernel's own fp32
+    activation, padding rows untouched, sampled activation entries against
+    single-dot-product oracle values."""
+    print("full swiglu contiguous", flush=True)
+    A, sa, B, sb, mi = fullsize_contiguous(False)
+    M, G, N = A.shape[0], B.shape[0], B.shape[1]
+    I = N // 2
+    Q, sq, act = prefilled((), M, I)
+    fg.grouped_contiguous_swiglu_quant(to_dev(A), to_dev(np.ascontiguousarray(sa.T)), to_dev(B), to_dev(sb),
+                                       to_dev(mi), Q, sq, act)
+    torch.cuda.synchronize()
+    Qh, sqh, acth = Q.cpu().numpy(), sq.cpu().numpy().T, act.cpu().numpy()
+    valid = mi >= 0
+    assert np.all(Qh[~valid] == Q_FILL) and np.all(acth[~valid] == F_FILL) and np.all(sqh[~valid] == F_FILL)
+    codes, scales = oracle.quantize_act_1x128(acth[valid])
+    assert np.array_equal(codes, Qh[valid]) and np.array_equal(scales, sqh[valid])
+    rng = np.random.default_rng(351)
+    for g in range(G):
+        rows_g = np.nonzero(mi == g)[0]
+        rows = rng.choice(rows_g, 24)
+        cols = rng.integers(0, I, 24)
+        gate_cols = (cols // 128) * 256 + cols % 128
+        gate = oracle.ref_entries(A, sa, B[g], sb[g], rows, gate_cols)
+        up = oracle.ref_entries(A, sa, B[g], sb[g], rows, gate_cols + 128)
+        r = check_f32(acth[rows, cols], oracle.silu(gate) * up)
         assert r["ok"], (g, r)
