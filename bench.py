@@ -25,9 +25,14 @@ the power-of-two-scale entry points (E8M0 scales applied by the matrix core),
 with operands quantised by the power-of-two quantisers; `moe_swiglu_quant`
 times the fused first-projection calls (GEMM + SiLU gate + 1x128 E4M3
 re-quantisation, fp32 scales, no activation copy) on the two MoE workloads.
-The headline and `per_workload` entries also carry `warm_kernel_us`: the same
-calls on a single input copy, resident in the MALL where it fits (reported
-beside the cold numbers, never as `value`).
+The headline takes exactly --warmup untimed steps (default 4000, ~115 ms of
+its kernel: the clocks take tens of milliseconds of sustained load to settle);
+every other entry warms up for at least --workload-warmup-ms (default 200) and
+times max(5, steps/10) launches.
+Each entry also gives `launch_us_median_min_max` from one event pair per
+launch (a separate pass). The headline and `per_workload` entries also carry
+`warm_kernel_us`: the same calls on a single input copy, resident in the MALL
+where it fits (reported beside the cold numbers, never as `value`).
 """
 import argparse
 import ctypes
@@ -54,8 +59,11 @@ ORDER = ["dense_small", "dense_skinny", "contiguous", "masked", "dense_ffn"]
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    # the default warm-up (~115 ms of the headline kernel) lets the clocks settle
+    ap.add_argument("--warmup", type=int, default=4000)
+    ap.add_argument("--workload-warmup-ms", type=float, default=200.0,
+                    help="minimum untimed warm-up per non-headline measurement")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline workload (for profiling runs)")
@@ -203,11 +211,23 @@ def make_step(op, copies, fg, torch):
     return step
 
 
-def timed_steps(step, steps, warmup, torch):
-    """(wall ms, HIP-event ms) per step over `steps` steps after `warmup`."""
+def timed_steps(step, steps, warmup, torch, warmup_ms=0.0):
+    """(wall ms, HIP-event ms) per step over `steps` steps after `warmup`
+    untimed steps, extended until at least `warmup_ms` of them have run (the
+    GPU's clocks take tens of milliseconds of sustained load to settle: the
+    first launches after setup run up to ~35% slower)."""
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    done = warmup
+    if warmup_ms > 0:
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < warmup_ms:
+            for _ in range(max(1, warmup)):
+                step(done)
+                done += 1
+            torch.cuda.synchronize()
+    warmup = done
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -221,22 +241,33 @@ def timed_steps(step, steps, warmup, torch):
     return (t1 - t0) * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
 
-def time_workload(name, steps, warmup, fg, torch, pow2=False, fused=False, warm=False):
+def time_workload(name, steps, warmup, fg, torch, pow2=False, fused=False, warm=False, warmup_ms=0.0):
     """Cold timing: steps rotate over input copies that together exceed the
     MALL, so every launch reads its operands from HBM. warm=True also times the
     same calls on one copy (operands resident in the 256 MB MALL when they fit)."""
     op = gpu_operands(name, fg, torch, pow2, fused)
     copies = replicate(op, torch)
     step = make_step(op, copies, fg, torch)
-    wall_ms, kern_ms = timed_steps(step, steps, warmup, torch)
+    wall_ms, kern_ms = timed_steps(step, steps, warmup, torch, warmup_ms)
     warm_ms = None
     if warm:
         warm_ms = timed_steps(make_step(op, copies[:1], fg, torch), steps, warmup, torch)[1]
+    # per-launch spread: a separate pass with one event pair per launch (the
+    # averaged timing above records no events between launches)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(warmup + steps + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_launch = sorted(a.elapsed_time(b) for a, b in evs)
     layout = {"dense": 0, "contiguous": 1, "masked": 2}[op["kind"]]
     if fused:
         layout |= fg.SELECT_SWIGLU_QUANT
     bm, bn, grid = fg.select_config(layout, op["M"], op["N"], op["K"], op["G"])
     res = dict(op=op, copies=len(copies), wall_ms=wall_ms, kern_ms=kern_ms, warm_ms=warm_ms,
+               launch_ms=(per_launch[len(per_launch) // 2], per_launch[0], per_launch[-1]),
                tile=f"{bm}x{bn}", grid=grid, bytes=algorithmic_bytes(op))
     del copies
     return res
@@ -251,7 +282,8 @@ def summarize(r):
                kernel_us=round(r["kern_ms"] * 1e3, 2), tflops=round(tflops, 1),
                pct_fp8_peak=round(100 * kt / PEAK_FP8_TFLOPS, 2),
                hbm_gbps=round(r["bytes"] / (r["kern_ms"] * 1e-3) / 1e9, 1),
-               input_copies=r["copies"])
+               input_copies=r["copies"],
+               launch_us_median_min_max=[round(x * 1e3, 2) for x in r["launch_ms"]])
     if r.get("warm_ms"):
         out.update(warm_kernel_us=round(r["warm_ms"] * 1e3, 2),
                    warm_pct_fp8_peak=round(100 * op["flop"] / (r["warm_ms"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2))
@@ -459,8 +491,8 @@ def main():
         for name in ORDER:
             if name == args.workload:
                 continue
-            r = time_workload(name, max(5, args.steps // 2), max(2, args.warmup // 2), fg, torch,
-                              head_pow2, warm=True)
+            r = time_workload(name, max(5, args.steps // 10), 5, fg, torch, head_pow2, warm=True,
+                              warmup_ms=args.workload_warmup_ms)
             per[name] = summarize(r)
             del r
             torch.cuda.empty_cache()
@@ -468,8 +500,8 @@ def main():
     if not args.headline_only and not args.no_pow2:
         per_pow2 = {}
         for name in ORDER:
-            r = time_workload(name, max(5, args.steps // 2), max(2, args.warmup // 2), fg, torch,
-                              not head_pow2)
+            r = time_workload(name, max(5, args.steps // 10), 5, fg, torch, not head_pow2,
+                              warmup_ms=args.workload_warmup_ms)
             per_pow2[name] = summarize(r)
             del r
             torch.cuda.empty_cache()
@@ -478,8 +510,8 @@ def main():
     if not args.headline_only and not args.no_pow2:
         fused = {}
         for name in ("contiguous", "masked"):
-            r = time_workload(name, max(5, args.steps // 2), max(2, args.warmup // 2), fg, torch,
-                              False, True)
+            r = time_workload(name, max(5, args.steps // 10), 5, fg, torch, False, True,
+                              warmup_ms=args.workload_warmup_ms)
             fused[name] = summarize(r)
             del r
             torch.cuda.empty_cache()
