@@ -15,7 +15,7 @@ using Cfg0 = TileCfg<256, 256, 4, 2, 2, false, 2, false, 3>;   // large dense / 
 using Cfg1 = TileCfg<256, 128, 4, 2, 3, false, 2, false, 3>;
 using Cfg2 = TileCfg<128, 256, 2, 4, 3, false, 2, false, 3>;   // contiguous (BM | 128)
 using Cfg3 = TileCfg<128, 128, 2, 2, 4, false, 3, false, 3>;
-using Cfg4 = TileCfg<64, 112, 4, 1, 6, true, 6, true, 3, 3>;     // skinny M, HBM-bound
+using Cfg4 = TileCfg<64, 112, 4, 1, 4, true, 3, true, 3, 4>;     // skinny M, HBM-bound
 using Cfg5 = TileCfg<256, 112, 4, 1, 3, true, 2, false, 3>;    // masked decode, HBM-bound
 using Cfg6 = TileCfg<256, 224, 4, 2, 2, true, 2, false, 3>;    // N = 7168: 32 column tiles
 }  // namespace tiles
