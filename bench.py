@@ -6,9 +6,10 @@ tile scheduling, staging, E4M3 MFMA per 128-wide K-block, promotion with
 sa*sb into the FP32 master accumulator, bf16 epilogue) over one batch of
 seeded synthetic input that is already resident in device memory.
 
-Headline workload: dense D = A . B^T with M=256, N=7168, K=7168, A and B drawn
-N(0,1) (1% of A's rows scaled x50), quantised on the GPU to E4M3 with fp32
-scales per 1x128 (A) and 128x128 (B) block, bf16 output.
+Headline workload (the large dense FFN GEMM, the compute-bound case): dense
+D = A . B^T with M=8192, N=7168, K=18432, A and B drawn N(0,1), quantised on
+the GPU to E4M3 with fp32 scales per 1x128 (A) and 128x128 (B) block, bf16
+output. `--workload` names another of the five workloads instead.
 
 The inputs are replicated into enough copies to exceed the 256 MB last-level
 (MALL) cache, and consecutive steps rotate through the copies, so each launch
@@ -17,25 +18,31 @@ streams its operands from HBM instead of re-reading a cached copy.
 Prints ONE JSON line. `value` is TFLOP/s of useful work (2*M*N*K over rows that
 have an output) per wall-clock second over the timed steps. `roofline` is for
 the GEMM kernel, from HIP events recorded on the launch stream around the timed
-steps. `cpu_baseline` is the CPU oracle (dequantise + fp64 GEMM) timed on this
-host. `per_workload` repeats the measurement for the other workloads (the small
-dense case, MoE contiguous, MoE masked, the large dense FFN GEMM) unless
---headline-only is given; `per_workload_pow2` measures every workload again on
-the power-of-two-scale entry points (E8M0 scales applied by the matrix core),
-with operands quantised by the power-of-two quantisers; `moe_swiglu_quant`
-times the fused first-projection calls (GEMM + SiLU gate + 1x128 E4M3
-re-quantisation, fp32 scales, no activation copy) on the two MoE workloads.
-The headline takes exactly --warmup untimed steps (default 4000, ~115 ms of
-its kernel: the clocks take tens of milliseconds of sustained load to settle);
-every other entry warms up for at least --workload-warmup-ms (default 200) and
-times max(5, steps/10) launches.
-Each entry also gives `launch_us_median_min_max` from one event pair per
-launch (a separate pass). The headline and `per_workload` entries also carry
-`warm_kernel_us`: the same calls on a single input copy, resident in the MALL
-where it fits (reported beside the cold numbers, never as `value`).
+steps: MFMA-bound workloads against the published 5.0 PFLOP/s dense FP8 peak,
+HBM-bound ones against 8 TB/s. `cpu_baseline` is the CPU oracle (dequantise +
+fp64 GEMM) timed on this host on a bounded sample of the headline workload;
+`cpu_baseline_per_config` does the same for every workload (the whole problem
+where one oracle call takes seconds, else a stated sample). `per_workload`
+repeats the GPU measurement for the other workloads (the small dense case, the
+skinny dense case, MoE contiguous, MoE masked) unless --headline-only is given;
+`per_workload_pow2` measures every workload again on the power-of-two-scale
+entry points (E8M0 scales applied by the matrix core), with operands quantised
+by the power-of-two quantisers; `moe_swiglu_quant` times the fused
+first-projection calls (GEMM + SiLU gate + 1x128 E4M3 re-quantisation, fp32
+scales, no activation copy) on the two MoE workloads.
+
+Every measurement, the headline included, first runs --warmup untimed steps
+and then keeps launching until at least --warmup-ms (default 200) of untimed
+work has run, whatever --warmup says: the GPU's clocks take tens of
+milliseconds of sustained load to settle. Non-headline entries then time
+max(5, steps/10) launches. Each entry also gives `launch_us_median_min_max`
+from one event pair per launch (a separate pass), and `warm_kernel_us`: the
+same calls on a single input copy, resident in the MALL where it fits
+(reported beside the cold numbers, never as `value`).
 """
 import argparse
 import ctypes
+import functools
 import json
 import math
 import os
@@ -46,24 +53,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_FP8_TFLOPS = 256 * 2.4e9 * 8192 / 1e12    # 5033: 256 CUs x 2.4 GHz x 8192 FLOP/clk/CU
+# published MI355X dense FP8 MFMA peak (256 CUs x 2.4 GHz x 8192 FLOP/clk/CU = 5033 at the nominal clock)
+PEAK_FP8_TFLOPS = 5000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_02_amd", "csrc", f)
                   for f in ("fg_kernel.hpp", "fg_e4m3.hpp", "fg_tiles.hpp", "fg_launch.hip", "fg_host.hip")]
 PEAK_HBM_GBPS = 8000.0                          # HBM3E, 8 TB/s
 MALL_BYTES = 256 << 20
-HEADLINE = "dense_skinny"
+HEADLINE = "dense_ffn"
 ORDER = ["dense_small", "dense_skinny", "contiguous", "masked", "dense_ffn"]
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    # the default warm-up (~115 ms of the headline kernel) lets the clocks settle
-    ap.add_argument("--warmup", type=int, default=4000)
-    ap.add_argument("--workload-warmup-ms", type=float, default=200.0,
-                    help="minimum untimed warm-up per non-headline measurement")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-ms", "--workload-warmup-ms", dest="warmup_ms", type=float, default=200.0,
+                    help="minimum untimed warm-up of every measurement, the headline included "
+                         "(the clocks take tens of milliseconds of sustained load to settle)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline workload (for profiling runs)")
@@ -74,7 +82,9 @@ def parse():
     ap.add_argument("--no-pow2", action="store_true",
                     help="skip the per-workload measurements of the power-of-two path")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="target CPU time for the oracle baseline sample")
+                    help="target CPU time for the headline's oracle baseline sample")
+    ap.add_argument("--config-cpu-seconds", type=float, default=2.0,
+                    help="target CPU time for each per-config oracle baseline")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="summarise rocprofv3 output under DIR (trace/, fetch/, write/ subfolders "
                          "from --kernel-trace --stats, --pmc FETCH_SIZE, --pmc WRITE_SIZE runs of "
@@ -86,6 +96,14 @@ def parse():
 
 
 # --------------------------------------------------------------------- inputs
+@functools.lru_cache(maxsize=1)
+def _workload(name):
+    """Seeded fp32 inputs of one workload (kept while consecutive measurements
+    use it; one workload at a time)."""
+    import workloads
+    return workloads.make(name)
+
+
 def gpu_operands(name, fg, torch, pow2=False, fused=False):
     """Seeded fp32 inputs (numpy) -> device -> E4M3 + scales by the library's
     quantisers (pow2: the power-of-two-scale quantisers). Returns a dict of
@@ -93,7 +111,7 @@ def gpu_operands(name, fg, torch, pow2=False, fused=False):
     import numpy as np
     import workloads
 
-    w = workloads.make(name)
+    w = _workload(name)
     dev = torch.device("cuda", 0)
     a = torch.from_numpy(w["a"]).to(dev)
     b = torch.from_numpy(w["b"]).to(dev)
@@ -265,7 +283,8 @@ def time_workload(name, steps, warmup, fg, torch, pow2=False, fused=False, warm=
     layout = {"dense": 0, "contiguous": 1, "masked": 2}[op["kind"]]
     if fused:
         layout |= fg.SELECT_SWIGLU_QUANT
-    bm, bn, grid = fg.select_config(layout, op["M"], op["N"], op["K"], op["G"])
+    bm, bn = fg.select_config(op["M"], op["N"], op["K"], op["G"], layout)
+    grid = fg.select_grid(op["M"], op["N"], op["K"], op["G"], layout)
     res = dict(op=op, copies=len(copies), wall_ms=wall_ms, kern_ms=kern_ms, warm_ms=warm_ms,
                launch_ms=(per_launch[len(per_launch) // 2], per_launch[0], per_launch[-1]),
                tile=f"{bm}x{bn}", grid=grid, bytes=algorithmic_bytes(op))
@@ -291,35 +310,71 @@ def summarize(r):
 
 
 # --------------------------------------------------------------- CPU baseline
-def cpu_baseline(name, target_s):
-    """The oracle as it stands (dequantise to fp64 + one fp64 GEMM per expert),
-    timed on this host for the headline workload. Inputs are quantised by the
-    oracle outside the timed region."""
-    import numpy as np
-    import oracle
-    import workloads
+# What the oracle baseline runs per workload: None = the whole problem (one
+# oracle call takes at most a few seconds); for the large dense FFN GEMM a
+# block of the output -- its first `rows` rows and `cols` columns -- over the
+# full K, since one call on the whole problem would take minutes of CPU time.
+CPU_SAMPLES = {"dense_small": None, "dense_skinny": None, "contiguous": None, "masked": None,
+               "dense_ffn": dict(rows=1024, cols=1792)}
 
-    w = workloads.make(name)
-    if w["kind"] != "dense":
-        raise ValueError("CPU baseline is defined for the dense headline workload")
-    A, sa = oracle.quantize_act_1x128(w["a"])
-    B, sb = oracle.quantize_weight_128x128(w["b"])
+
+def oracle_case(name):
+    """(call, useful FLOP of one call, description) for one oracle call on the
+    workload or its sample. Inputs are quantised by the oracle before any
+    timing (chunked over threads; the same codes as the serial quantisers)."""
+    import oracle
+    from oracle.parallel import quantize_act_1x128_par, quantize_weight_128x128_par
+
+    w = _workload(name)
+    samp = CPU_SAMPLES[name]
+    if w["kind"] == "dense":
+        a, b = w["a"], w["b"]
+        M, N, K = a.shape[0], b.shape[0], a.shape[1]
+        desc = f"whole problem {M}x{N}x{K}"
+        if samp:
+            a, b = a[:samp["rows"]], b[:samp["cols"]]
+            desc = (f"output rows 0..{a.shape[0] - 1} x columns 0..{b.shape[0] - 1} of the {M}x{N} output, "
+                    f"full K = {K}")
+        A, sa = quantize_act_1x128_par(a)
+        B, sb = quantize_weight_128x128_par(b)
+        flop = 2.0 * A.shape[0] * B.shape[0] * K
+        return (lambda: oracle.ref_dense(A, sa, B, sb)), flop, desc
+    import workloads
     flop = workloads.useful_flop(w)
+    A, sa = quantize_act_1x128_par(w["a"])
+    B, sb = quantize_weight_128x128_par(w["b"])
+    if w["kind"] == "contiguous":
+        mi = w["m_indices"]
+        desc = f"whole problem: {B.shape[0]} experts, {int((mi >= 0).sum())} rows, N={B.shape[1]}, K={A.shape[1]}"
+        return (lambda: oracle.ref_contiguous(A, sa, B, sb, mi)), flop, desc
+    mm = w["masked_m"]
+    desc = (f"whole problem: {B.shape[0]} experts, M_max={A.shape[1]}, {int(mm.sum())} valid rows, "
+            f"N={B.shape[1]}, K={A.shape[2]}")
+    return (lambda: oracle.ref_masked(A, sa, B, sb, mm)), flop, desc
+
+
+def oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(name, target_s):
+    """The oracle as it stands (dequantise to fp64 + one fp64 numpy GEMM per
+    expert), timed on this host with time.perf_counter: repeated calls until
+    target_s seconds (at least one call, at most 50)."""
+    call, flop, desc = oracle_case(name)
     reps, spent = 0, 0.0
     while reps == 0 or (spent < target_s and reps < 50):
         t0 = time.perf_counter()
-        oracle.ref_dense(A, sa, B, sb)
+        call()
         spent += time.perf_counter() - t0
         reps += 1
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = len(os.sched_getaffinity(0))
-    return {"value": round(flop * reps / spent / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"full {name} problem ({A.shape[0]}x{B.shape[0]}x{A.shape[1]}), "
-                      f"{reps} repetition(s), {spent:.1f} s; dequantise + fp64 numpy GEMM; "
+    return {"value": round(flop * reps / spent / 1e12, 5), "unit": "TFLOP/s", "cores": oracle_threads(),
+            "kind": "oracle", "seconds_per_call": round(spent / reps, 4),
+            "sample": f"{name}: {desc}; {reps} call(s), {spent:.1f} s; dequantise + fp64 numpy GEMM; "
                       f"host cpus {len(os.sched_getaffinity(0))}"}
 
 
@@ -451,7 +506,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU path is not built)", file=sys.stderr)
+              "(nothing here uses a second GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
     import moe_grouped_gemm_02_amd as fg
@@ -461,11 +516,41 @@ def main():
         sys.exit(1)
     fg.lib()
     head_pow2 = args.scales == "pow2"
-    # (no warm launches in --headline-only runs: a profiler's average for the
-    # kernel must be the cold launches' alone)
-    head = time_workload(args.workload, args.steps, args.warmup, fg, torch, head_pow2,
-                         warm=not args.headline_only)
-    hs = summarize(head)
+    full = not args.headline_only
+    sub_steps = max(5, args.steps // 10)
+    per, per_pow2, fused, cpu_cfg = {}, {}, {}, {}
+    head = None
+    # the headline first, then the other workloads one at a time (each
+    # workload's inputs are generated once for its GPU and CPU measurements)
+    for name in [args.workload] + [n for n in ORDER if n != args.workload]:
+        is_head = name == args.workload
+        if is_head:
+            # (no warm launches in --headline-only runs: a profiler's average for
+            # the kernel must be the cold launches' alone)
+            head = time_workload(name, args.steps, args.warmup, fg, torch, head_pow2, warm=full,
+                                 warmup_ms=args.warmup_ms)
+            per[name] = summarize(head)
+        elif full:
+            r = time_workload(name, sub_steps, args.warmup, fg, torch, head_pow2, warm=True,
+                              warmup_ms=args.warmup_ms)
+            per[name] = summarize(r)
+            del r
+        torch.cuda.empty_cache()
+        if full and not args.no_pow2:
+            r = time_workload(name, sub_steps, args.warmup, fg, torch, not head_pow2, warmup_ms=args.warmup_ms)
+            per_pow2[name] = summarize(r)
+            del r
+            torch.cuda.empty_cache()
+        if full and name in ("contiguous", "masked"):
+            r = time_workload(name, sub_steps, args.warmup, fg, torch, False, True, warmup_ms=args.warmup_ms)
+            fused[name] = summarize(r)
+            del r
+            torch.cuda.empty_cache()
+        if not args.no_cpu_baseline and (is_head or full):
+            cpu_cfg[name] = cpu_baseline(name, args.cpu_seconds if is_head else args.config_cpu_seconds)
+    _workload.cache_clear()
+
+    hs = per[args.workload]
     op = head["op"]
     value = op["flop"] / (head["wall_ms"] * 1e-3) / 1e12
     kern_s = head["kern_ms"] * 1e-3
@@ -478,51 +563,16 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4), "traffic": None}
     else:
-        roof = {"bound": "mfma", "achieved": round(achieved_tflops, 1), "peak": round(PEAK_FP8_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP8_TFLOPS, 4),
-                "traffic": None}
-    roof.update(kernel_us=hs["kernel_us"], algorithmic_bytes=head["bytes"],
-                flop=op["flop"], fp8_peak_frac=round(achieved_tflops / PEAK_FP8_TFLOPS, 4))
+        roof = {"bound": "mfma", "achieved": round(achieved_tflops, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None}
+    roof.update(kernel_us=hs["kernel_us"], algorithmic_bytes=head["bytes"], flop=op["flop"],
+                hbm_frac=round(achieved_gbps / PEAK_HBM_GBPS, 4))
     del head
     torch.cuda.empty_cache()
-
-    per = {args.workload: hs}
-    if not args.headline_only:
-        for name in ORDER:
-            if name == args.workload:
-                continue
-            r = time_workload(name, max(5, args.steps // 10), 5, fg, torch, head_pow2, warm=True,
-                              warmup_ms=args.workload_warmup_ms)
-            per[name] = summarize(r)
-            del r
-            torch.cuda.empty_cache()
-    per_pow2 = None
-    if not args.headline_only and not args.no_pow2:
-        per_pow2 = {}
-        for name in ORDER:
-            r = time_workload(name, max(5, args.steps // 10), 5, fg, torch, not head_pow2,
-                              warmup_ms=args.workload_warmup_ms)
-            per_pow2[name] = summarize(r)
-            del r
-            torch.cuda.empty_cache()
-
-    fused = None
-    if not args.headline_only and not args.no_pow2:
-        fused = {}
-        for name in ("contiguous", "masked"):
-            r = time_workload(name, max(5, args.steps // 10), 5, fg, torch, False, True,
-                              warmup_ms=args.workload_warmup_ms)
-            fused[name] = summarize(r)
-            del r
-            torch.cuda.empty_cache()
 
     if args.calibrate_copy_mb:
         copy_calibration(args.calibrate_copy_mb, torch)
     roof["traffic"] = measured_traffic(args.workload) if not head_pow2 else None
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.workload, args.cpu_seconds)
 
     line = {
         "metric": "FP8 TFLOPS (dense + grouped MoE) and % of MI355X dense FP8 MFMA peak",
@@ -531,6 +581,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_ms_floor": args.warmup_ms,
         "ms_per_step": round(hs["us_per_call"] / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -544,10 +595,11 @@ def main():
                    "out": "bf16", "tile": hs["tile"], "input_copies": hs["input_copies"],
                    "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2)},
         "roofline": roof,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_cfg.get(args.workload),
+        "cpu_baseline_per_config": cpu_cfg or None,
         "per_workload": per,
-        ("per_workload_fp32" if head_pow2 else "per_workload_pow2"): per_pow2,
-        "moe_swiglu_quant": fused,
+        ("per_workload_fp32" if head_pow2 else "per_workload_pow2"): per_pow2 or None,
+        "moe_swiglu_quant": fused or None,
     }
     print(json.dumps(line), flush=True)
 

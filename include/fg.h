@@ -61,9 +61,9 @@ enum {
   FG_EINVAL = -1,        /* bad argument: null pointer, negative size,
                             K not a multiple of 128, N not a multiple of
                             8, misalignment,
-                            G < 1 for a grouped call, unknown tile
-                            or scale kind; N not a multiple of 256
-                            for the fused calls */
+                            G < 1 for a grouped call, unknown
+                            layout or scale kind; N not a multiple
+                            of 256 for the fused calls */
   FG_EUNSUPPORTED = -2,  /* current device is not gfx950 */
   FG_ELAUNCH = -3,       /* the kernel launch failed (hipGetLastError) */
   FG_EDEVICE = -4        /* a HIP runtime query failed */
@@ -172,7 +172,7 @@ int fg_grouped_masked_pow2(const void* A, const float* sa, const void* B, const 
  * Rows without output (M tail, masked rows >= masked_m[g], contiguous rows
  * with m_indices = -1) are not written in Q, sq or act. No bf16 H is written.
  * The call uses 256-column tiles only (fg_select_config with
- * FG_SELECT_SWIGLU_QUANT); a forced tile of another width gives FG_EINVAL.
+ * FG_SELECT_SWIGLU_QUANT).
  */
 int fg_gemm_fp8_nt_swiglu_quant(const void* A, const float* sa, const void* B, const float* sb,
                                 void* Q, float* sq, float* act, int M, int N, int K, int scales,
@@ -186,27 +186,33 @@ int fg_grouped_masked_swiglu_quant(const void* A, const float* sa, const void* B
 
 /*
  * Tile configuration the library would launch for a problem, computed on the
- * host from sizes only (no device access, usable without a GPU). Tiles are
- * chosen from a fixed table to minimise wave quantisation over `num_cus`
- * compute units, the point the zwzgs.cn DeepGEMM page makes in "Technical
- * details > non-standard block sizes" (M=256, N=7168 on 132 SMs: 112 tiles of
- * 128x128 versus 128 of 128x112).
- *   layout  FG_LAYOUT_*, optionally | FG_SELECT_SWIGLU_QUANT;
- *   M = total rows (dense, contiguous) or M_max (masked);
- *   G = experts (1 for dense). num_cus <= 0 means the library's default (256).
- * Writes the tile's rows/cols to *bm / *bn and the number of workgroups the
- * launch would use to *grid (any of the three may be NULL).
+ * host from sizes only (pure: no device access, no state; usable without a
+ * GPU). Tiles are chosen from a fixed table to minimise wave quantisation
+ * over `num_cus` compute units, the point the zwzgs.cn DeepGEMM page makes in
+ * "Technical details > non-standard block sizes" (M=256, N=7168 on 132 SMs:
+ * 112 tiles of 128x128 versus 128 of 128x112), weighed against each tile's
+ * per-K-block cost.
+ *   M       total rows (dense, contiguous) or M_max (masked);
+ *   N, K    as for the GEMM calls (N % 8 == 0, K % 128 == 0 need not hold
+ *           here: the choice is made for any non-negative sizes);
+ *   G       experts (ignored for dense; >= 1 for the grouped layouts);
+ *   layout  FG_LAYOUT_*, optionally | FG_SELECT_SWIGLU_QUANT for the tile the
+ *           fused SiLU-gate epilogue would use;
+ *   num_cus compute units to fill; <= 0 means the library's default (256,
+ *           MI355X).
+ * Writes the tile's rows / columns to *bm / *bn (either may be NULL).
+ * Returns FG_OK, or FG_EINVAL for an unknown layout, a negative size or
+ * G < 1 with a grouped layout.
  */
-int fg_select_config(int layout, int M, int N, int K, int G, int num_cus,
-                     int* bm, int* bn, int* grid);
+int fg_select_config(int M, int N, int K, int G, int layout, int num_cus, int* bm, int* bn);
 
-/* Force a tile configuration for subsequent calls (bm x bn must be one of the
- * compiled tiles), or restore automatic selection with bm = bn = 0. Intended
- * for tests and tile sweeps; process-wide, not thread-safe. A call (and
- * fg_select_config) returns FG_EINVAL if the forced tile does not suit it: a
- * fused call needs 256 columns; a contiguous call takes 256-row tiles only
- * while its device-side tile list fits (M <= 262144 rows, G <= 32767). */
-int fg_force_tile(int bm, int bn);
+/*
+ * Number of workgroups the launch for the same problem would use (same
+ * arguments and errors as fg_select_config): one per output tile, except
+ * the contiguous layout on 256-row tiles, whose workgroups walk a tile list
+ * persistently (at most one per compute unit).
+ */
+int fg_select_grid(int M, int N, int K, int G, int layout, int num_cus, int* grid);
 
 /*
  * fp32 -> E4M3 quantisation producing this library's operand layouts
@@ -224,12 +230,15 @@ int fg_force_tile(int bm, int bn);
 int fg_quant_act_1x128(const float* x, void* q, float* sa, int batch, int M, int K,
                        hipStream_t stream);
 
-/* Weights, 128x128 blocks: w [rows][K] fp32 with rows % 128 == 0 (a grouped
- *   weight [G][N][K] is rows = G*N), q [rows][K] E4M3, sb [rows/128][K/128]
- *   fp32 (= [G][N/128][K/128]). Weights with N not a multiple of 128 are
- *   quantised by the caller (the last row block's scale from its N mod 128
- *   rows). */
-int fg_quant_weight_128x128(const float* w, void* q, float* sb, int rows, int K,
+/* Weights, 128x128 blocks: w [G][N][K] fp32 (16-byte aligned; G = 1 for a
+ *   dense weight), q [G][N][K] E4M3, sb [G][ceil(N/128)][K/128] fp32 (the
+ *   GEMM's sb layout). K % 128 == 0; N >= 0 is arbitrary: when N is not a
+ *   multiple of 128 the last row block of each expert holds the remaining
+ *   N mod 128 rows, its amax and scale come from those rows alone (the same
+ *   block the GEMM scales with the last sb row), and nothing past row N is
+ *   read or written. The 2kiu.com explainer, section 4.3, names boundary
+ *   handling for shapes that do not fill a block. */
+int fg_quant_weight_128x128(const float* w, void* q, float* sb, int G, int N, int K,
                             hipStream_t stream);
 
 /* Power-of-two variants of the two quantisers (same arguments, layouts and
@@ -240,7 +249,7 @@ int fg_quant_weight_128x128(const float* w, void* q, float* sb, int rows, int K,
  * name (2kiu.com explainer, section 7) without defining. */
 int fg_quant_act_1x128_pow2(const float* x, void* q, float* sa, int batch, int M, int K,
                             hipStream_t stream);
-int fg_quant_weight_128x128_pow2(const float* w, void* q, float* sb, int rows, int K,
+int fg_quant_weight_128x128_pow2(const float* w, void* q, float* sb, int G, int N, int K,
                                  hipStream_t stream);
 
 /* Static, human-readable description of a return code. */

@@ -33,41 +33,55 @@ class FGError(RuntimeError):
     pass
 
 
+def _declare(L):
+    """Argument and return types of every entry point of include/fg.h."""
+    vp, fp, ip, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+    ipp = ctypes.POINTER(ctypes.c_int)
+    L.fg_gemm_fp8_nt.argtypes = [vp, fp, vp, fp, vp, i, i, i, vp]
+    L.fg_grouped_contiguous.argtypes = [vp, fp, vp, fp, vp, ip, i, i, i, i, vp]
+    L.fg_grouped_masked.argtypes = [vp, fp, vp, fp, vp, ip, i, i, i, i, vp]
+    L.fg_select_config.argtypes = [i, i, i, i, i, i, ipp, ipp]
+    L.fg_select_grid.argtypes = [i, i, i, i, i, i, ipp]
+    L.fg_quant_act_1x128.argtypes = [vp, vp, vp, i, i, i, vp]
+    L.fg_quant_weight_128x128.argtypes = [vp, vp, vp, i, i, i, vp]
+    L.fg_gemm_fp8_nt_pow2.argtypes = L.fg_gemm_fp8_nt.argtypes
+    L.fg_grouped_contiguous_pow2.argtypes = L.fg_grouped_contiguous.argtypes
+    L.fg_grouped_masked_pow2.argtypes = L.fg_grouped_masked.argtypes
+    L.fg_quant_act_1x128_pow2.argtypes = L.fg_quant_act_1x128.argtypes
+    L.fg_quant_weight_128x128_pow2.argtypes = L.fg_quant_weight_128x128.argtypes
+    L.fg_gemm_fp8_nt_swiglu_quant.argtypes = [vp, fp, vp, fp, vp, fp, fp, i, i, i, i, vp]
+    L.fg_grouped_contiguous_swiglu_quant.argtypes = [vp, fp, vp, fp, vp, fp, fp, ip, i, i, i, i, i, vp]
+    L.fg_grouped_masked_swiglu_quant.argtypes = [vp, fp, vp, fp, vp, fp, fp, ip, i, i, i, i, i, vp]
+    L.fg_strerror.argtypes = [i]
+    L.fg_strerror.restype = ctypes.c_char_p
+    for name in ENTRY_POINTS:
+        if name != "fg_strerror":
+            getattr(L, name).restype = ctypes.c_int
+    return L
+
+
+ENTRY_POINTS = ("fg_gemm_fp8_nt", "fg_grouped_contiguous", "fg_grouped_masked",
+                "fg_select_config", "fg_select_grid", "fg_quant_act_1x128",
+                "fg_quant_weight_128x128", "fg_gemm_fp8_nt_pow2", "fg_grouped_contiguous_pow2",
+                "fg_grouped_masked_pow2", "fg_quant_act_1x128_pow2",
+                "fg_quant_weight_128x128_pow2", "fg_gemm_fp8_nt_swiglu_quant",
+                "fg_grouped_contiguous_swiglu_quant", "fg_grouped_masked_swiglu_quant",
+                "fg_strerror")
+
+
+def load(path):
+    """ctypes handle of a build of the library at `path`, with its entry points
+    declared (raises ImportError if the file is missing)."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m moe_grouped_gemm_02_amd.build`")
+    return _declare(ctypes.CDLL(path))
+
+
 def lib():
     """Load libfg.so (built in-tree by ``moe_grouped_gemm_02_amd.build``)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(
-                f"{LIB_PATH} is missing: build it with `python -m moe_grouped_gemm_02_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, fp, ip, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
-        L.fg_gemm_fp8_nt.argtypes = [vp, fp, vp, fp, vp, i, i, i, vp]
-        L.fg_grouped_contiguous.argtypes = [vp, fp, vp, fp, vp, ip, i, i, i, i, vp]
-        L.fg_grouped_masked.argtypes = [vp, fp, vp, fp, vp, ip, i, i, i, i, vp]
-        L.fg_select_config.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
-                                       ctypes.POINTER(i)]
-        L.fg_force_tile.argtypes = [i, i]
-        L.fg_quant_act_1x128.argtypes = [vp, vp, vp, i, i, i, vp]
-        L.fg_quant_weight_128x128.argtypes = [vp, vp, vp, i, i, vp]
-        L.fg_gemm_fp8_nt_pow2.argtypes = L.fg_gemm_fp8_nt.argtypes
-        L.fg_grouped_contiguous_pow2.argtypes = L.fg_grouped_contiguous.argtypes
-        L.fg_grouped_masked_pow2.argtypes = L.fg_grouped_masked.argtypes
-        L.fg_quant_act_1x128_pow2.argtypes = L.fg_quant_act_1x128.argtypes
-        L.fg_quant_weight_128x128_pow2.argtypes = L.fg_quant_weight_128x128.argtypes
-        L.fg_gemm_fp8_nt_swiglu_quant.argtypes = [vp, fp, vp, fp, vp, fp, fp, i, i, i, i, vp]
-        L.fg_grouped_contiguous_swiglu_quant.argtypes = [vp, fp, vp, fp, vp, fp, fp, ip, i, i, i, i, i, vp]
-        L.fg_grouped_masked_swiglu_quant.argtypes = [vp, fp, vp, fp, vp, fp, fp, ip, i, i, i, i, i, vp]
-        L.fg_strerror.argtypes = [i]
-        L.fg_strerror.restype = ctypes.c_char_p
-        for name in ("fg_gemm_fp8_nt", "fg_grouped_contiguous", "fg_grouped_masked",
-                     "fg_select_config", "fg_force_tile", "fg_quant_act_1x128",
-                     "fg_quant_weight_128x128", "fg_gemm_fp8_nt_pow2", "fg_grouped_contiguous_pow2",
-                     "fg_grouped_masked_pow2", "fg_quant_act_1x128_pow2",
-                     "fg_quant_weight_128x128_pow2", "fg_gemm_fp8_nt_swiglu_quant",
-                     "fg_grouped_contiguous_swiglu_quant", "fg_grouped_masked_swiglu_quant"):
-            getattr(L, name).restype = ctypes.c_int
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
 
 
@@ -282,17 +296,20 @@ def grouped_masked_swiglu_quant(A, sa, B, sb, masked_m, Q=None, sq=None, act=Non
     return Q, sq, act
 
 
-def select_config(layout, M, N, K, G=1, num_cus=0):
-    """(bm, bn, grid) the library would launch; host-only, no device access."""
-    bm, bn, grid = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(lib().fg_select_config(layout, M, N, K, G, num_cus, ctypes.byref(bm),
-                                  ctypes.byref(bn), ctypes.byref(grid)), "fg_select_config")
-    return bm.value, bn.value, grid.value
+def select_config(M, N, K, G=1, layout=LAYOUT_DENSE, num_cus=0):
+    """(bm, bn): the tile the library would launch for the problem (layout
+    optionally | SELECT_SWIGLU_QUANT); host-only, no device access."""
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    _check(lib().fg_select_config(M, N, K, G, layout, num_cus, ctypes.byref(bm), ctypes.byref(bn)),
+           "fg_select_config")
+    return bm.value, bn.value
 
 
-def force_tile(bm=0, bn=0):
-    """Force a compiled tile shape for later calls; (0, 0) restores automatic choice."""
-    _check(lib().fg_force_tile(bm, bn), "fg_force_tile")
+def select_grid(M, N, K, G=1, layout=LAYOUT_DENSE, num_cus=0):
+    """Workgroups the launch for the problem would use; host-only."""
+    grid = ctypes.c_int()
+    _check(lib().fg_select_grid(M, N, K, G, layout, num_cus, ctypes.byref(grid)), "fg_select_grid")
+    return grid.value
 
 
 def quant_act_1x128(x, q=None, sa=None):
@@ -328,7 +345,8 @@ def _quant_act(fn, x, q, sa):
 
 def quant_weight_128x128(w, q=None, sb=None):
     """fp32 weights [N, K] (or [G, N, K]) -> (E4M3 codes, sb) with one scale per
-    128x128 block; sb is [N/128, K/128] ([G, N/128, K/128])."""
+    128x128 block; sb is [ceil(N/128), K/128] ([G, ceil(N/128), K/128]). N need
+    not be a multiple of 128: the last row block then holds N mod 128 rows."""
     return _quant_weight("fg_quant_weight_128x128", w, q, sb)
 
 
@@ -341,17 +359,17 @@ def _quant_weight(fn, w, q, sb):
     torch = _torch()
     if w.dim() not in (2, 3):
         raise ValueError("w must be [N, K] or [G, N, K]")
+    G = w.shape[0] if w.dim() == 3 else 1
     N, K = w.shape[-2], w.shape[-1]
-    if N % 128 or K % 128:
-        raise ValueError("N and K must be multiples of 128")
-    rows = w.numel() // K
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
     _dev(w, "w", tuple(w.shape), torch.float32)
-    sb_shape = tuple(w.shape[:-2]) + (N // 128, K // 128)
+    sb_shape = tuple(w.shape[:-2]) + (-(-N // 128), K // 128)
     if q is None:
         q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
     if sb is None:
         sb = torch.empty(sb_shape, dtype=torch.float32, device=w.device)
     _fp8(q, "q", tuple(w.shape))
     _dev(sb, "sb", sb_shape, torch.float32)
-    _check(getattr(lib(), fn)(_ptr(w), _ptr(q), _ptr(sb), rows, K, _stream(w)), fn)
+    _check(getattr(lib(), fn)(_ptr(w), _ptr(q), _ptr(sb), G, N, K, _stream(w)), fn)
     return q, sb

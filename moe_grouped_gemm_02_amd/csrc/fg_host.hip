@@ -52,7 +52,12 @@ constexpr Tile kTiles[] = {{256, 256, Cfg0::W, 0.75}, {256, 128, Cfg1::W, 0.75},
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kDefaultCUs = 256;
 
-std::atomic<int> g_forced_tile{-1};
+#ifdef FG_TESTING
+// Test-only build (libfg_testing.so): a per-thread tile override that the
+// test suite sets around a call to run one compiled tile on a problem the
+// cost model would give another. The product library has no such state.
+thread_local int t_forced_tile = -1;
+#endif
 
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
@@ -106,9 +111,11 @@ long launch_grid(int layout, int M, int N, int G, const Tile& t, int cus) {
 // block per row); bn256 restricts the choice to those.
 constexpr double kTileFixedCycles = 4000.0;
 int pick_tile(int layout, int M, int N, int K, int G, int cus, bool bn256 = false) {
-  const int forced = g_forced_tile.load(std::memory_order_relaxed);
+#ifdef FG_TESTING
+  const int forced = t_forced_tile;
   if (forced >= 0)
     return (!bn256 || kTiles[forced].bn == 256) && tile_allowed(layout, M, G, kTiles[forced]) ? forced : -1;
+#endif
   int best = -1;
   double best_cost = 0.0;
   const double kblocks = K / 128;
@@ -179,7 +186,7 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   if (st != FG_OK) return st;
 
   const int ti = pick_tile(layout, M, N, K, G, cus, fused != nullptr);
-  if (ti < 0) return FG_EINVAL;   // a forced tile this call cannot use
+  if (ti < 0) return FG_EINVAL;   // (test build) a forced tile this call cannot use
   const Tile& t = kTiles[ti];
   Params p;
   p.A = static_cast<const uint8_t*>(A);
@@ -211,6 +218,20 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
     e = pow2 ? launch<true, fg::kEpiBf16>(layout, ti, p, grid, stream)
              : launch<false, fg::kEpiBf16>(layout, ti, p, grid, stream);
   return e == hipSuccess ? FG_OK : FG_ELAUNCH;
+}
+
+// Tile index and grid for a problem, from sizes only.
+int select_tile(int M, int N, int K, int G, int layout, int num_cus, int* ti, long* grid) {
+  const bool fused = (layout & FG_SELECT_SWIGLU_QUANT) != 0;
+  layout &= ~FG_SELECT_SWIGLU_QUANT;
+  if (layout < FG_LAYOUT_DENSE || layout > FG_LAYOUT_MASKED) return FG_EINVAL;
+  if (M < 0 || N < 0 || K < 0 || (layout != FG_LAYOUT_DENSE && G < 1)) return FG_EINVAL;
+  if (layout == FG_LAYOUT_DENSE) G = 1;
+  const int cus = num_cus > 0 ? num_cus : kDefaultCUs;
+  *ti = pick_tile(layout, M, N, K, G, cus, fused);
+  if (*ti < 0) return FG_EINVAL;
+  *grid = launch_grid(layout, M, N, G, kTiles[*ti], cus);
+  return FG_OK;
 }
 
 }  // namespace
@@ -290,40 +311,48 @@ int fg_grouped_masked_swiglu_quant(const void* A, const float* sa, const void* B
              scales == FG_SCALES_POW2, &out);
 }
 
-int fg_select_config(int layout, int M, int N, int K, int G, int num_cus, int* bm, int* bn,
-                     int* grid) {
-  const bool fused = (layout & FG_SELECT_SWIGLU_QUANT) != 0;
-  layout &= ~FG_SELECT_SWIGLU_QUANT;
-  if (layout < FG_LAYOUT_DENSE || layout > FG_LAYOUT_MASKED) return FG_EINVAL;
-  if (M < 0 || N < 0 || K < 0 || (layout != FG_LAYOUT_DENSE && G < 1)) return FG_EINVAL;
-  if (layout == FG_LAYOUT_DENSE) G = 1;
-  const int cus = num_cus > 0 ? num_cus : kDefaultCUs;
-  const int ti = pick_tile(layout, M, N, K, G, cus, fused);
-  if (ti < 0) return FG_EINVAL;
+int fg_select_config(int M, int N, int K, int G, int layout, int num_cus, int* bm, int* bn) {
+  int ti = -1;
+  long grid = 0;
+  const int rc = select_tile(M, N, K, G, layout, num_cus, &ti, &grid);
+  if (rc != FG_OK) return rc;
   if (bm) *bm = kTiles[ti].bm;
   if (bn) *bn = kTiles[ti].bn;
-  if (grid) *grid = (int)launch_grid(layout, M, N, G, kTiles[ti], cus);
   return FG_OK;
 }
 
-int fg_force_tile(int bm, int bn) {
+int fg_select_grid(int M, int N, int K, int G, int layout, int num_cus, int* grid) {
+  int ti = -1;
+  long g = 0;
+  const int rc = select_tile(M, N, K, G, layout, num_cus, &ti, &g);
+  if (rc != FG_OK) return rc;
+  if (grid) *grid = g > 0x7fffffffL ? 0x7fffffff : (int)g;
+  return FG_OK;
+}
+
+#ifdef FG_TESTING
+// Test build only: force tile bm x bn (one of the compiled tiles) for this
+// thread's later calls, or restore the automatic choice with bm = bn = 0. A
+// call that cannot use the forced tile returns FG_EINVAL.
+int fgt_force_tile(int bm, int bn) {
   if (bm == 0 && bn == 0) {
-    g_forced_tile.store(-1);
+    t_forced_tile = -1;
     return FG_OK;
   }
   for (int i = 0; i < kNumTiles; ++i) {
     if (kTiles[i].bm == bm && kTiles[i].bn == bn) {
-      g_forced_tile.store(i);
+      t_forced_tile = i;
       return FG_OK;
     }
   }
   return FG_EINVAL;
 }
+#endif
 
 const char* fg_strerror(int code) {
   switch (code) {
     case FG_OK: return "success";
-    case FG_EINVAL: return "invalid argument (null pointer, negative size, K not a multiple of 128, N not a multiple of 8 (256 for the fused epilogue), K < 128, misaligned pointer, G < 1, unknown scale kind or tile)";
+    case FG_EINVAL: return "invalid argument (null pointer, negative size, K not a multiple of 128, N not a multiple of 8 (256 for the fused epilogue), K < 128, misaligned pointer, G < 1, unknown layout or scale kind)";
     case FG_EUNSUPPORTED: return "unsupported device (gfx950 required)";
     case FG_ELAUNCH: return "kernel launch failed";
     case FG_EDEVICE: return "HIP device query failed";

@@ -64,23 +64,32 @@ __global__ __launch_bounds__(256) void quant_act_1x128(const float* __restrict__
 }
 
 // 128x128 blocks: one 256-thread workgroup per block, 16 float4 per thread.
-// w [R][K] (R = G*N rows, a multiple of 128) -> q [R][K], sb [R/128][K/128].
+// w [G][N][K] -> q [G][N][K], sb [G][ceil(N/128)][K/128]. When N is not a
+// multiple of 128 the last row block of each expert holds the remaining
+// N mod 128 rows: its amax (and so its scale) comes from those rows alone, and
+// nothing past row N is read or written.
 __global__ __launch_bounds__(256) void quant_weight_128x128(const float* __restrict__ w,
                                                             uint8_t* __restrict__ q,
-                                                            float* __restrict__ sb, int K, int pow2) {
-  __shared__ float red[8];
+                                                            float* __restrict__ sb, int N, int K, int pow2) {
+  __shared__ float red[4];
   const int KB = K / 128;
-  const long br = blockIdx.x / KB;
-  const int kb = blockIdx.x - (int)(br * KB);
+  const int NB = (N + 127) / 128;
+  const long blk = blockIdx.x;
+  const long gnb = blk / KB;          // (expert, row block) pair
+  const int kb = (int)(blk - gnb * KB);
+  const long g = gnb / NB;
+  const int nb = (int)(gnb - g * NB);
   const int t = threadIdx.x;
   const int col = (t & 31) * 4;       // 32 threads cover one 128-wide row
-  const int r0 = t >> 5;              // 8 rows per pass, 16 passes
+  const int r0 = nb * 128 + (t >> 5); // 8 rows per pass, 16 passes
+  const float* wg = w + g * (long)N * K;
+  uint8_t* qg = q + g * (long)N * K;
   float4 v[16];
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const long row = br * 128 + r0 + i * 8;
-    v[i] = *(const float4*)(w + row * K + (long)kb * 128 + col);
+    const int row = r0 + i * 8;
+    v[i] = row < N ? *(const float4*)(wg + (long)row * K + (long)kb * 128 + col) : make_float4(0.f, 0.f, 0.f, 0.f);
     m = fmaxf(m, amax4(v[i]));
   }
 #pragma unroll
@@ -92,10 +101,10 @@ __global__ __launch_bounds__(256) void quant_weight_128x128(const float* __restr
   if (pow2) s = pow2_up(s);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const long row = br * 128 + r0 + i * 8;
-    *(uint32_t*)(q + row * K + (long)kb * 128 + col) = encode4(v[i], s, pow2);
+    const int row = r0 + i * 8;
+    if (row < N) *(uint32_t*)(qg + (long)row * K + (long)kb * 128 + col) = encode4(v[i], s, pow2);
   }
-  if (t == 0) sb[br * KB + kb] = s;
+  if (t == 0) sb[gnb * KB + kb] = s;
 }
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -112,14 +121,14 @@ int quant_act(const float* x, void* q, float* sa, int batch, int M, int K, hipSt
   return hipGetLastError() == hipSuccess ? FG_OK : FG_ELAUNCH;
 }
 
-int quant_weight(const float* w, void* q, float* sb, int rows, int K, hipStream_t stream, int pow2) {
-  if (rows < 0 || rows % 128 || K < 128 || K % 128) return FG_EINVAL;
-  if (rows == 0) return FG_OK;
+int quant_weight(const float* w, void* q, float* sb, int G, int N, int K, hipStream_t stream, int pow2) {
+  if (G < 0 || N < 0 || K < 128 || K % 128) return FG_EINVAL;
+  if (G == 0 || N == 0) return FG_OK;
   if (!w || !q || !sb || !aligned(w, 16) || !aligned(q, 4) || !aligned(sb, 4)) return FG_EINVAL;
-  const long grid = (long)(rows / 128) * (K / 128);
+  const long grid = (long)G * ((N + 127) / 128) * (K / 128);
   if (grid > 0x7fffffffL) return FG_EINVAL;
   hipLaunchKernelGGL(quant_weight_128x128, dim3((unsigned)grid), dim3(256), 0, stream, w,
-                     static_cast<uint8_t*>(q), sb, K, pow2);
+                     static_cast<uint8_t*>(q), sb, N, K, pow2);
   return hipGetLastError() == hipSuccess ? FG_OK : FG_ELAUNCH;
 }
 
@@ -133,9 +142,9 @@ int fg_quant_act_1x128(const float* x, void* q, float* sa, int batch, int M, int
   return quant_act(x, q, sa, batch, M, K, stream, 0);
 }
 
-int fg_quant_weight_128x128(const float* w, void* q, float* sb, int rows, int K,
+int fg_quant_weight_128x128(const float* w, void* q, float* sb, int G, int N, int K,
                             hipStream_t stream) {
-  return quant_weight(w, q, sb, rows, K, stream, 0);
+  return quant_weight(w, q, sb, G, N, K, stream, 0);
 }
 
 int fg_quant_act_1x128_pow2(const float* x, void* q, float* sa, int batch, int M, int K,
@@ -143,9 +152,9 @@ int fg_quant_act_1x128_pow2(const float* x, void* q, float* sa, int batch, int M
   return quant_act(x, q, sa, batch, M, K, stream, 1);
 }
 
-int fg_quant_weight_128x128_pow2(const float* w, void* q, float* sb, int rows, int K,
+int fg_quant_weight_128x128_pow2(const float* w, void* q, float* sb, int G, int N, int K,
                                  hipStream_t stream) {
-  return quant_weight(w, q, sb, rows, K, stream, 1);
+  return quant_weight(w, q, sb, G, N, K, stream, 1);
 }
 
 }  // extern "C"

@@ -95,12 +95,39 @@ def quant_inputs(shape, seed):
     return x
 
 
+@functools.lru_cache(maxsize=1)
+def workload(name):
+    """The named workload's fp32 inputs (shared by consecutive full-size tests;
+    treat as read-only)."""
+    return workloads.make(name)
+
+
+def fullsize_quantized(name, pow2=False):
+    """A named workload quantised by the oracle (chunked over threads: the same
+    codes and scales as the serial quantisers), natural layouts: dense
+    (A, sa, B, sb), contiguous (A, sa, B, sb, m_indices), masked
+    (A [G, M_max, K], sa [G, M_max, K/128], B, sb, masked_m)."""
+    from oracle.parallel import quantize_act_1x128_par, quantize_weight_128x128_par
+    w = workload(name)
+    A, sa = quantize_act_1x128_par(w["a"], pow2)
+    B, sb = quantize_weight_128x128_par(w["b"], pow2)
+    if w["kind"] == "contiguous":
+        return A, sa, B, sb, w["m_indices"]
+    if w["kind"] == "masked":
+        return A, sa, B, sb, w["masked_m"]
+    return A, sa, B, sb
+
+
 @functools.lru_cache(maxsize=2)
 def fullsize_contiguous(pow2=False):
     """The contiguous MoE workload (8 experts, N 4096, K 7168) quantised by the
     oracle: (A, sa, B, sb, m_indices), natural layouts; computed once per scale
     kind and shared by the full-size tests (treat as read-only)."""
-    w = workloads.make("contiguous")
-    A, sa = oracle.quantize_act_1x128(w["a"], pow2)
-    B, sb = oracle.quantize_weight_128x128(w["b"], pow2)
-    return A, sa, B, sb, w["m_indices"]
+    return fullsize_quantized("contiguous", pow2)
+
+
+@functools.lru_cache(maxsize=2)
+def fullsize_contiguous_ref(pow2=False):
+    """The oracle's full D of the contiguous workload and its valid-row mask."""
+    A, sa, B, sb, mi = fullsize_contiguous(pow2)
+    return oracle.ref_contiguous(A, sa, B, sb, mi)

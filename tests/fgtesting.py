@@ -1,0 +1,50 @@
+"""Test-only tile override.
+
+The product library (libfg.so) picks every call's tile itself and holds no
+state that one caller could change for another. The test suite needs to run
+each compiled tile on problems the cost model would give another one, so the
+build also links libfg_testing.so: the same kernel objects, with host code
+built with FG_TESTING, which adds
+
+    int fgt_force_tile(int bm, int bn);   /* per calling thread; 0, 0 = automatic */
+
+``forced_tile(bm, bn)`` routes the package's calls through that library for the
+duration of a ``with`` block (on this thread's override) and restores the
+product library afterwards.
+"""
+import contextlib
+import ctypes
+import os
+
+import moe_grouped_gemm_02_amd as fg
+
+TESTING_LIB_PATH = os.path.join(os.path.dirname(fg.LIB_PATH), "libfg_testing.so")
+_tlib = None
+
+
+def testing_lib():
+    global _tlib
+    if _tlib is None:
+        L = fg.load(TESTING_LIB_PATH)
+        L.fgt_force_tile.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.fgt_force_tile.restype = ctypes.c_int
+        _tlib = L
+    return _tlib
+
+
+@contextlib.contextmanager
+def forced_tile(bm, bn):
+    """Run the package's calls inside the block on tile bm x bn (None: the
+    automatic choice, still through the testing library)."""
+    L = testing_lib()
+    saved = fg.lib()
+    if bm is not None:
+        rc = L.fgt_force_tile(bm, bn)
+        if rc != 0:
+            raise fg.FGError(f"fgt_force_tile({bm}, {bn}): {fg.strerror(rc)}")
+    fg._lib = L
+    try:
+        yield
+    finally:
+        fg._lib = saved
+        L.fgt_force_tile(0, 0)

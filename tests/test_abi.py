@@ -8,6 +8,7 @@ import re
 import pytest
 
 import moe_grouped_gemm_02_amd as fg
+from fgtesting import forced_tile as forced, testing_lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fg.h")
@@ -23,7 +24,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fg_gemm_fp8_nt", "fg_grouped_contiguous", "fg_grouped_masked",
-              "fg_select_config", "fg_strerror", "fg_quant_act_1x128", "fg_quant_weight_128x128",
+              "fg_select_config", "fg_select_grid", "fg_strerror", "fg_quant_act_1x128", "fg_quant_weight_128x128",
               "fg_gemm_fp8_nt_pow2", "fg_grouped_contiguous_pow2", "fg_grouped_masked_pow2",
               "fg_quant_act_1x128_pow2", "fg_quant_weight_128x128_pow2",
               "fg_gemm_fp8_nt_swiglu_quant", "fg_grouped_contiguous_swiglu_quant",
@@ -94,12 +95,15 @@ def test_quant_validation():
     L = fg.lib()
     assert L.fg_quant_act_1x128(GOOD, GOOD, GOOD, 1, 64, 100, None) == EINVAL
     assert L.fg_quant_act_1x128(BAD, GOOD, GOOD, 1, 64, 128, None) == EINVAL
-    assert L.fg_quant_weight_128x128(GOOD, GOOD, GOOD, 100, 128, None) == EINVAL
+    assert L.fg_quant_weight_128x128(GOOD, GOOD, GOOD, 1, 100, 100, None) == EINVAL    # K % 128
+    assert L.fg_quant_weight_128x128(GOOD, GOOD, GOOD, -1, 128, 128, None) == EINVAL   # G < 0
+    assert L.fg_quant_weight_128x128(BAD, GOOD, GOOD, 1, 72, 128, None) == EINVAL      # misaligned w
+    assert L.fg_quant_weight_128x128(None, None, None, 2, 0, 128, None) == OK           # N = 0
     assert L.fg_quant_act_1x128(None, None, None, 1, 0, 128, None) == OK
     assert L.fg_quant_act_1x128_pow2(GOOD, GOOD, GOOD, 1, 64, 100, None) == EINVAL
     assert L.fg_quant_act_1x128_pow2(BAD, GOOD, GOOD, 1, 64, 128, None) == EINVAL
-    assert L.fg_quant_weight_128x128_pow2(GOOD, GOOD, GOOD, 100, 128, None) == EINVAL
-    assert L.fg_quant_weight_128x128_pow2(None, None, None, 0, 128, None) == OK
+    assert L.fg_quant_weight_128x128_pow2(GOOD, GOOD, GOOD, 1, 128, 100, None) == EINVAL
+    assert L.fg_quant_weight_128x128_pow2(None, None, None, 0, 128, 128, None) == OK
 
 
 def test_fused_validation():
@@ -122,17 +126,41 @@ def test_fused_validation():
 def test_fused_select_config_uses_256_column_tiles():
     for layout, M, N, K, G in [(0, 256, 7168, 7168, 1), (0, 8192, 7168, 18432, 1), (1, 9472, 4096, 7168, 8),
                                (2, 256, 7168, 2048, 16), (0, 64, 512, 256, 1)]:
-        bm, bn, grid = fg.select_config(layout | fg.SELECT_SWIGLU_QUANT, M, N, K, G)
+        bm, bn = fg.select_config(M, N, K, G, layout | fg.SELECT_SWIGLU_QUANT)
         assert bn == 256
         if layout == 1:
             assert 128 % bm == 0 or bm == 256
+
+
+def test_select_config_argument_order():
+    # int fg_select_config(M, N, K, G, layout, num_cus, *bm, *bn): the masked
+    # decode problem (G = 16 experts of M_max = 256 rows) and the skinny dense
+    # one give different tiles, so a swapped argument shows
+    L = fg.lib()
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    assert L.fg_select_config(256, 7168, 7168, 1, 0, 256, ctypes.byref(bm), ctypes.byref(bn)) == OK
+    assert (bm.value, bn.value) == (64, 112)
+    assert L.fg_select_config(256, 7168, 2048, 16, 2, 0, ctypes.byref(bm), None) == OK
+    assert bm.value == 256
+    grid = ctypes.c_int()
+    assert L.fg_select_grid(256, 7168, 7168, 1, 0, 256, ctypes.byref(grid)) == OK
+    assert grid.value == 256
+    assert L.fg_select_grid(256, 7168, 2048, 16, 2, 0, None) == OK
+    # errors: unknown layout, negative size, G < 1 for a grouped layout
+    assert L.fg_select_config(256, 7168, 7168, 1, 3, 0, None, None) == EINVAL
+    assert L.fg_select_config(-1, 7168, 7168, 1, 0, 0, None, None) == EINVAL
+    assert L.fg_select_config(256, 7168, 7168, 0, 1, 0, None, None) == EINVAL
+    assert L.fg_select_grid(256, 7168, 7168, 0, 2, 0, ctypes.byref(grid)) == EINVAL
+    # dense ignores G
+    assert L.fg_select_config(256, 7168, 7168, 0, 0, 0, ctypes.byref(bm), None) == OK
 
 
 def test_select_config_fills_the_machine():
     # every choice must be a compiled tile and give a sane grid
     for layout, M, N, K, G in [(0, 256, 7168, 7168, 1), (0, 8192, 7168, 18432, 1), (0, 128, 256, 512, 1),
                                (1, 9472, 4096, 7168, 8), (2, 256, 7168, 2048, 16)]:
-        bm, bn, grid = fg.select_config(layout, M, N, K, G)
+        bm, bn = fg.select_config(M, N, K, G, layout)
+        grid = fg.select_grid(M, N, K, G, layout)
         assert bm > 0 and bn > 0 and N % 16 == 0
         tiles = -(-M // bm) * -(-N // bn) * (G if layout == 2 else 1)
         if layout == 1 and bm == 256:
@@ -155,23 +183,48 @@ def test_select_config_picks_the_measured_best_tiles():
     # the big dense and masked problems (fewer re-reads of A and B; 256x224
     # splits N = 7168 into 32 whole column tiles), and the widest tile with
     # BM | 128 for the contiguous layout.
-    assert fg.select_config(0, 256, 7168, 7168, 1)[:2] == (64, 112)
-    assert fg.select_config(1, 9472, 4096, 7168, 8)[:2] == (256, 224)
-    assert fg.select_config(2, 256, 7168, 2048, 16)[:2] in ((256, 224), (256, 256))
-    assert fg.select_config(0, 8192, 7168, 18432, 1)[:2] in ((256, 128), (256, 256), (256, 224))
+    assert fg.select_config(256, 7168, 7168, 1, 0) == (64, 112)
+    assert fg.select_config(9472, 4096, 7168, 8, 1) == (256, 224)
+    assert fg.select_config(256, 7168, 2048, 16, 2) in ((256, 224), (256, 256))
+    assert fg.select_config(8192, 7168, 18432, 1, 0) in ((256, 128), (256, 256), (256, 224))
 
 
 def test_select_config_rejects_bad_layout():
     with pytest.raises(fg.FGError):
-        fg.select_config(7, 128, 128, 128)
+        fg.select_config(128, 128, 128, 1, 7)
 
 
-def test_force_tile_roundtrip():
-    fg.force_tile(128, 128)
-    assert fg.select_config(0, 8192, 7168, 18432)[:2] == (128, 128)
-    fg.force_tile(0, 0)
+def test_product_library_has_no_tile_override():
+    # the tile override is a test-build hook (libfg_testing.so), never part of
+    # the product library's state
+    L = ctypes.CDLL(fg.LIB_PATH)
+    for name in ("fg_force_tile", "fgt_force_tile"):
+        assert not hasattr(L, name), name
+
+
+def test_testing_library_override_is_per_call_site():
+    with forced(128, 128):
+        assert fg.select_config(8192, 7168, 18432, 1, 0) == (128, 128)
+    # restored on exit, and the product library never saw it
+    assert fg.select_config(8192, 7168, 18432, 1, 0) != (128, 128)
     with pytest.raises(fg.FGError):
-        fg.force_tile(96, 96)
+        with forced(96, 96):
+            pass
+
+
+def test_testing_override_is_per_thread():
+    import threading
+    seen = {}
+
+    def other():
+        seen["other"] = testing_lib().fg_select_config(8192, 7168, 18432, 1, 0, 0, ctypes.byref(bm), None), bm.value
+
+    bm = ctypes.c_int()
+    with forced(128, 128):
+        t = threading.Thread(target=other)
+        t.start()
+        t.join()
+    assert seen["other"][0] == OK and seen["other"][1] != 128
 
 
 def test_contiguous_256_row_tiles_only_within_the_tile_list():
@@ -179,15 +232,12 @@ def test_contiguous_256_row_tiles_only_within_the_tile_list():
     # LDS (at most 2048 blocks of 128 rows, experts < 32768); beyond that the
     # choice falls back to tiles of at most 128 rows, and a forced 256-row tile
     # is refused.
-    assert fg.select_config(1, 2048 * 128, 4096, 7168, 8)[0] == 256
-    assert fg.select_config(1, 2048 * 128 + 1, 4096, 7168, 8)[0] <= 128
-    assert fg.select_config(1, 9472, 4096, 7168, 32768)[0] <= 128
-    fg.force_tile(256, 224)
-    try:
-        assert fg.select_config(1, 9472, 4096, 7168, 8)[:2] == (256, 224)
+    assert fg.select_config(2048 * 128, 4096, 7168, 8, 1)[0] == 256
+    assert fg.select_config(2048 * 128 + 1, 4096, 7168, 8, 1)[0] <= 128
+    assert fg.select_config(9472, 4096, 7168, 32768, 1)[0] <= 128
+    with forced(256, 224):
+        assert fg.select_config(9472, 4096, 7168, 8, 1) == (256, 224)
         with pytest.raises(fg.FGError):
-            fg.select_config(1, 2048 * 128 + 1, 4096, 7168, 8)
+            fg.select_config(2048 * 128 + 1, 4096, 7168, 8, 1)
         # dense and masked have no such limit
-        assert fg.select_config(0, 2048 * 128 + 1, 4096, 7168, 1)[:2] == (256, 224)
-    finally:
-        fg.force_tile(0, 0)
+        assert fg.select_config(2048 * 128 + 1, 4096, 7168, 1, 0) == (256, 224)

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 import moe_grouped_gemm_02_amd as fg
+from fgtesting import forced_tile as forced
 from fgtest import SENTINEL, d_bits, dense_inputs, new_out, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -37,11 +38,8 @@ def run_case(mi, G, N, K, seed, tile):
     B, sb = oracle.quantize_weight_128x128(b)
     Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
     D = new_out((M, N))
-    fg.force_tile(*tile)
-    try:
+    with forced(*tile):
         fg.grouped_contiguous(Ad, sad, Bd, sbd, D, to_dev(mi))
-    finally:
-        fg.force_tile(0, 0)
     torch.cuda.synchronize()
     # ids outside [0, G) are padding: no output, not written
     mi_ref = np.where((mi >= 0) & (mi < G), mi, -1)

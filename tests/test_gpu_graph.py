@@ -4,12 +4,15 @@ graph here is replayed several times, with eager fills, eager calls of the same
 entry point into other buffers and synchronisations between the replays, and
 every replay must reproduce the eager result bit for bit, including the rows the
 call must leave untouched."""
+import contextlib
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import moe_grouped_gemm_02_amd as fg
+from fgtesting import forced_tile as forced
 from fgtest import (SENTINEL, d_bits, dense_inputs, make_contiguous, make_dense, make_masked,
                     masked_inputs, new_out, to_dev)
 
@@ -76,9 +79,7 @@ def test_graph_contiguous(tile):
     mid = to_dev(mi)
     M = A.shape[0]
     D, D2 = new_out((M, 384)), new_out((M, 384))
-    if tile:
-        fg.force_tile(*tile)
-    try:
+    with (forced(*tile) if tile else contextlib.nullcontext()):
         replay_matches_eager(lambda o: fg.grouped_contiguous(Ad, sad, Bd, sbd, o[0], mid), [D],
                              lambda o: [fill_sentinel(x) for x in o], [D2])
         # same graph, new routing: every expert id rotated, rows stay in place
@@ -91,8 +92,6 @@ def test_graph_contiguous(tile):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-    finally:
-        fg.force_tile(0, 0)
     ref, valid = oracle.ref_contiguous(A, sa, B, sb, mi2)
     r = oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
     assert r["ok"], r

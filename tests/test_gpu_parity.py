@@ -7,6 +7,7 @@ import torch
 
 import oracle
 import moe_grouped_gemm_02_amd as fg
+from fgtesting import forced_tile as forced
 from fgtest import (SENTINEL, d_bits, dense_inputs, dev, make_contiguous, make_dense,
                     make_masked, masked_inputs, new_out, to_dev)
 
@@ -148,9 +149,8 @@ TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (64, 112), (256, 112), 
 @pytest.fixture
 def forced_tile(request):
     bm, bn = request.param
-    fg.force_tile(bm, bn)
-    yield bm, bn
-    fg.force_tile(0, 0)
+    with forced(bm, bn):
+        yield bm, bn
 
 
 @pytest.mark.parametrize("forced_tile", TILES, indirect=True, ids=lambda t: f"{t[0]}x{t[1]}")

@@ -9,6 +9,7 @@ import torch
 
 import oracle
 import moe_grouped_gemm_02_amd as fg
+from fgtesting import forced_tile as forced
 from fgtest import (SENTINEL, d_bits, dense_inputs, make_contiguous, make_dense, make_masked,
                     masked_inputs, new_out, quant_inputs, to_dev)
 
@@ -24,9 +25,8 @@ def forced_tile(request):
         yield None
         return
     bm, bn = request.param
-    fg.force_tile(bm, bn)
-    yield bm, bn
-    fg.force_tile(0, 0)
+    with forced(bm, bn):
+        yield bm, bn
 
 
 # ---------------------------------------------------------------- quantisers

@@ -70,3 +70,29 @@ def test_quant_rounding_boundaries_bit_exact(pow2):
     assert np.all(scales == 1.0)
     assert np.array_equal(sa.cpu().numpy().T, scales)
     assert np.array_equal(q.cpu().numpy(), codes)
+
+
+@pytest.mark.parametrize("pow2", [False, True], ids=["fp32_scales", "pow2_scales"])
+@pytest.mark.parametrize("shape", [(8, 256), (72, 384), (200, 128), (328, 640), (3, 72, 256), (2, 200, 384)])
+def test_weight_quant_ragged_n_bit_exact(shape, pow2):
+    """N not a multiple of 128: the last row block of each expert holds the
+    remaining N mod 128 rows and takes its scale from them alone. A spike in
+    the last (partial) block and a tiny-valued last block make its scale
+    differ from what a full block or a neighbour would give."""
+    print(f"weight quant ragged N {shape} pow2={pow2}", flush=True)
+    rng = np.random.default_rng(9)
+    w = rng.standard_normal(shape, dtype=np.float32)
+    flat = w.reshape(-1, shape[-2], shape[-1])
+    N = shape[-2]
+    last = (N - 1) // 128 * 128
+    flat[0, N - 1, 5] = 40.0                                  # spike in the partial block
+    flat[-1, last:, 128:256] *= np.float32(2.0 ** -20)        # tiny partial block
+    fn = fg.quant_weight_128x128_pow2 if pow2 else fg.quant_weight_128x128
+    wd = to_dev(w)
+    q = torch.full(shape, 0x5A, dtype=torch.uint8, device=wd.device)
+    q, sb = fn(wd, q=q)
+    torch.cuda.synchronize()
+    codes, scales = oracle.quantize_weight_128x128(w, pow2)
+    assert q.shape == codes.shape and sb.shape == scales.shape
+    assert np.array_equal(q.cpu().numpy(), codes)
+    assert np.array_equal(sb.cpu().numpy(), scales)

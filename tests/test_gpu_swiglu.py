@@ -21,9 +21,10 @@ import pytest
 import torch
 
 import oracle
-import workloads
 import moe_grouped_gemm_02_amd as fg
-from fgtest import fullsize_contiguous, make_contiguous, make_dense, make_masked, to_dev
+from fgtesting import forced_tile as forced
+from fgtest import (fullsize_contiguous, fullsize_contiguous_ref, fullsize_quantized, make_contiguous, make_dense,
+                    make_masked, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,9 +39,8 @@ def forced_tile(request):
         yield None
         return
     bm, bn = request.param
-    fg.force_tile(bm, bn)
-    yield bm, bn
-    fg.force_tile(0, 0)
+    with forced(bm, bn):
+        yield bm, bn
 
 
 def prefilled(lead, M, I):
@@ -144,12 +144,9 @@ def test_without_the_activation_output():
 def test_fused_rejects_narrow_tiles_and_bad_n():
     A, sa, B, sb = make_dense(64, 256, 128, 332)
     args = (to_dev(A), to_dev(np.ascontiguousarray(sa.T)), to_dev(B), to_dev(sb))
-    fg.force_tile(256, 128)
-    try:
+    with forced(256, 128):
         with pytest.raises(fg.FGError):
             fg.gemm_fp8_nt_swiglu_quant(*args)
-    finally:
-        fg.force_tile(0, 0)
     A2, sa2, B2, sb2 = make_dense(64, 384, 128, 333)
     with pytest.raises(ValueError):
         fg.gemm_fp8_nt_swiglu_quant(to_dev(A2), to_dev(np.ascontiguousarray(sa2.T)), to_dev(B2), to_dev(sb2))
@@ -158,19 +155,13 @@ def test_fused_rejects_narrow_tiles_and_bad_n():
 @SCALES
 def test_fullsize_masked_swiglu_quant(pow2):
     """The masked decode workload (16 experts, M_max 256, N 7168 -> I 3584,
-    K 2048) in the launch configuration the benchmark times: sampled act
-    entries against single-dot-product oracle values, codes and scales of every
-    valid row bit for bit, untouched rows in full."""
+    K 2048) in the launch configuration the benchmark times: every act entry
+    of every valid row against the oracle's silu(gate) * up of its full fp64
+    GEMM, codes and scales of every valid row bit for bit, untouched rows in
+    full."""
     print(f"full swiglu masked pow2={pow2}", flush=True)
-    w = workloads.make("masked")
-    G, M_max, K = w["a"].shape
-    A = np.empty((G, M_max, K), np.uint8)
-    sa = np.empty((G, M_max, K // 128), np.float32)
-    for g in range(G):
-        A[g], sa[g] = oracle.quantize_act_1x128(w["a"][g], pow2)
-    B, sb = oracle.quantize_weight_128x128(w["b"], pow2)
-    mm = w["masked_m"]
-    del w
+    A, sa, B, sb, mm = fullsize_quantized("masked", pow2)
+    G, M_max = A.shape[0], A.shape[1]
     N = B.shape[1]
     I = N // 2
     Q, sq, act = prefilled((G,), M_max, I)
@@ -178,53 +169,42 @@ def test_fullsize_masked_swiglu_quant(pow2):
                                    to_dev(B), to_dev(sb), to_dev(mm), Q, sq, act, pow2=pow2)
     torch.cuda.synchronize()
     Qh, sqh, acth = Q.cpu().numpy(), sq.cpu().numpy(), act.cpu().numpy()
-    rng = np.random.default_rng(341)
+    ref, valid = oracle.ref_masked(A, sa, B, sb, mm)
     for g in range(G):
-        m = int(np.clip(mm[g], 0, M_max))
-        valid = np.arange(M_max) < m
-        assert np.all(Qh[g][~valid] == Q_FILL) and np.all(acth[g][~valid] == F_FILL)
-        assert np.all(sqh[g].T[~valid] == F_FILL)
-        if m == 0:
-            continue
-        codes, scales = oracle.quantize_act_1x128(acth[g][:m], pow2)
-        assert np.array_equal(codes, Qh[g][:m]) and np.array_equal(scales, sqh[g].T[:m])
-        rows = rng.integers(0, m, 48)
-        cols = rng.integers(0, I, 48)
-        gate_cols = (cols // 128) * 256 + cols % 128
-        gate = oracle.ref_entries(A[g], sa[g], B[g], sb[g], rows, gate_cols)
-        up = oracle.ref_entries(A[g], sa[g], B[g], sb[g], rows, gate_cols + 128)
-        ref = oracle.silu(gate) * up
-        r = check_f32(acth[g][rows, cols], ref)
-        assert r["ok"], (g, r)
+        v = valid[g]
+        assert np.all(Qh[g][~v] == Q_FILL) and np.all(acth[g][~v] == F_FILL)
+        assert np.all(sqh[g].T[~v] == F_FILL)
+        if v.any():
+            codes, scales = oracle.quantize_act_1x128(acth[g][v], pow2)
+            assert np.array_equal(codes, Qh[g][v]) and np.array_equal(scales, sqh[g].T[v])
+    r = check_f32(acth[valid], oracle.swiglu_blocks(ref[valid]))
+    print(f"masked act: n_checked={int(valid.sum()) * I} {r}", flush=True)
+    assert r["ok"], r
 
 
-def test_fullsize_contiguous_swiglu_quant():
+@SCALES
+def test_fullsize_contiguous_swiglu_quant(pow2):
     """The contiguous MoE workload (8 experts, 9472 rows with padding, N 4096 ->
     I 2048, K 7168) on the automatically chosen tile (256x256, following the
     experts' runs of 128-row blocks): codes and scales of every row with an
     expert bit for bit against the oracle quantiser of the kernel's own fp32
-    activation, padding rows untouched, sampled activation entries against
-    single-dot-product oracle values."""
-    print("full swiglu contiguous", flush=True)
-    A, sa, B, sb, mi = fullsize_contiguous(False)
+    activation, padding rows untouched, every act entry of every row with an
+    expert against the oracle's silu(gate) * up of its full fp64 GEMM."""
+    print(f"full swiglu contiguous pow2={pow2}", flush=True)
+    A, sa, B, sb, mi = fullsize_contiguous(pow2)
     M, G, N = A.shape[0], B.shape[0], B.shape[1]
     I = N // 2
     Q, sq, act = prefilled((), M, I)
     fg.grouped_contiguous_swiglu_quant(to_dev(A), to_dev(np.ascontiguousarray(sa.T)), to_dev(B), to_dev(sb),
-                                       to_dev(mi), Q, sq, act)
+                                       to_dev(mi), Q, sq, act, pow2=pow2)
     torch.cuda.synchronize()
     Qh, sqh, acth = Q.cpu().numpy(), sq.cpu().numpy().T, act.cpu().numpy()
     valid = mi >= 0
     assert np.all(Qh[~valid] == Q_FILL) and np.all(acth[~valid] == F_FILL) and np.all(sqh[~valid] == F_FILL)
-    codes, scales = oracle.quantize_act_1x128(acth[valid])
+    codes, scales = oracle.quantize_act_1x128(acth[valid], pow2)
     assert np.array_equal(codes, Qh[valid]) and np.array_equal(scales, sqh[valid])
-    rng = np.random.default_rng(351)
-    for g in range(G):
-        rows_g = np.nonzero(mi == g)[0]
-        rows = rng.choice(rows_g, 24)
-        cols = rng.integers(0, I, 24)
-        gate_cols = (cols // 128) * 256 + cols % 128
-        gate = oracle.ref_entries(A, sa, B[g], sb[g], rows, gate_cols)
-        up = oracle.ref_entries(A, sa, B[g], sb[g], rows, gate_cols + 128)
-        r = check_f32(acth[rows, cols], oracle.silu(gate) * up)
-        assert r["ok"], (g, r)
+    ref, valid_ref = fullsize_contiguous_ref(pow2)
+    assert np.array_equal(valid, valid_ref)
+    r = check_f32(acth[valid], oracle.swiglu_blocks(ref[valid]))
+    print(f"contiguous act: n_checked={int(valid.sum()) * I} {r}", flush=True)
+    assert r["ok"], r

@@ -5,8 +5,10 @@ float8_e4m3fn cast, hand-built blocks with known scales, and the format's
 worst-case rounding error as a bound.
 """
 import numpy as np
+import pytest
 import torch
 
+import oracle
 from oracle import decode_table, quantize_act_1x128, quantize_weight_128x128
 
 DEC = decode_table()
@@ -101,3 +103,30 @@ def test_roundtrip_error_bound_and_no_nan():
     half_spacing = np.where(y < 2.0 ** -6, 2.0 ** -10, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 4))
     # x/scale is rounded to fp32 first; allow that one extra fp32 ulp
     assert np.all(np.abs(xr - x) <= (half_spacing * (1 + 2.0 ** -20)) * s)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_parallel_drivers_equal_serial(pow2):
+    """The chunked, thread-parallel drivers used for full-size inputs give the
+    serial quantisers' codes and scales exactly (blocks never straddle a chunk),
+    including a ragged last weight block and a batched activation."""
+    from oracle.parallel import quantize_act_1x128_par, quantize_weight_128x128_par
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((1100, 384), dtype=np.float32)
+    x[1099, 5] = 300.0
+    c1, s1 = quantize_act_1x128_par(x, pow2, chunk=256)
+    c2, s2 = oracle.quantize_act_1x128(x, pow2)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    xb = rng.standard_normal((3, 70, 256), dtype=np.float32)
+    c1, s1 = quantize_act_1x128_par(xb, pow2, chunk=32)
+    for b in range(3):
+        c2, s2 = oracle.quantize_act_1x128(xb[b], pow2)
+        assert np.array_equal(c1[b], c2) and np.array_equal(s1[b], s2)
+    w = rng.standard_normal((3, 584, 256), dtype=np.float32)
+    w[1, 583, 7] = 50.0
+    c1, s1 = quantize_weight_128x128_par(w, pow2, chunk=256)
+    c2, s2 = oracle.quantize_weight_128x128(w, pow2)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    c1, s1 = quantize_weight_128x128_par(w[0], pow2, chunk=128)
+    c2, s2 = oracle.quantize_weight_128x128(w[0], pow2)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
