@@ -32,7 +32,7 @@ first-projection calls (GEMM + SiLU gate + 1x128 E4M3 re-quantisation, fp32
 scales, no activation copy) on the two MoE workloads.
 
 Every measurement, the headline included, first runs --warmup untimed steps
-and then keeps launching until at least --warmup-ms (default 200) of untimed
+and then keeps launching until at least --warmup-ms (default 400) of untimed
 work has run, whatever --warmup says: the GPU's clocks take tens of
 milliseconds of sustained load to settle. Non-headline entries then time
 max(5, steps/10) launches. Each entry also gives `launch_us_median_min_max`
@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--warmup-ms", "--workload-warmup-ms", dest="warmup_ms", type=float, default=200.0,
+    ap.add_argument("--warmup-ms", "--workload-warmup-ms", dest="warmup_ms", type=float, default=400.0,
                     help="minimum untimed warm-up of every measurement, the headline included "
                          "(the clocks take tens of milliseconds of sustained load to settle)")
     ap.add_argument("--workload", default=HEADLINE)

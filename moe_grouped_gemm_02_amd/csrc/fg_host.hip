@@ -96,27 +96,74 @@ long launch_grid(int layout, int M, int N, int G, const Tile& t, int cus) {
   return most < cus ? most : cus;
 }
 
-// Picks the tile for a problem: the compiled shape with the smallest
-// estimated time, in CU cycles. One K-block of a tile costs the larger of its
+// Estimated cycles of one tile over kblocks K-blocks: the larger of its
 // matrix-core time (BM*BN*256 FLOP at 8192 FLOP/clk per CU, derated by the
 // tile's sustained fraction) and its global->LDS time ((BM+BN)*128 bytes at
 // the per-CU rate the GEMM sustains: ~24 B/clk with 4 issuing waves, ~30 with
-// 8); each tile adds a fixed prologue/epilogue cost. Tiles run in rounds over
-// the CUs, which carries the wave-quantisation loss the zwzgs.cn DeepGEMM
-// page describes ("non-standard block sizes": a tile count just above a
-// multiple of the SM count leaves most of the last round idle); partial tiles
-// carry their padding. Contiguous tiles must not straddle an aligned 128-row
-// expert block.
-// The fused SiLU-gate epilogue needs 256-column tiles (one gate and one up
-// block per row); bn256 restricts the choice to those.
+// 8) per K-block, plus a fixed prologue/epilogue cost.
 constexpr double kTileFixedCycles = 4000.0;
-int pick_tile(int layout, int M, int N, int K, int G, int cus, bool bn256 = false) {
+double tile_cycles(const Tile& t, double kblocks) {
+  const double t_mfma = (double)t.bm * t.bn * 256.0 / (8192.0 * t.eff);
+  const double t_mem = (double)(t.bm + t.bn) * 128.0 / (t.waves >= 8 ? 30.0 : 24.0);
+  return kblocks * (t_mfma > t_mem ? t_mfma : t_mem) + kTileFixedCycles;
+}
+
+// A launch plan: one compiled tile shape (index ti), or (split) the dense
+// two-shape kernel -- columns [0, n_split) on SplitWide tiles in whole rounds
+// (tiles_a of them), the rest on SplitNarrow tiles.
+struct Plan {
+  int ti = -1;
+  bool split = false;
+  int n_split = 0;
+  long tiles_a = 0;
+  long grid = 0;
+};
+constexpr int kWide = 0, kNarrow = 1;   // kTiles indices of SplitWide / SplitNarrow
+static_assert(SplitWide::BM == 256 && SplitWide::BN == 256 && SplitNarrow::BM == 256 && SplitNarrow::BN == 128,
+              "kTiles[kWide] / kTiles[kNarrow] describe the split kernel's tile shapes");
+
+// The dense split for columns [0, nc) on wide tiles and [nc, N) on narrow ones.
+Plan split_plan(int M, int N, int nc) {
+  Plan p;
+  p.split = true;
+  p.ti = kWide;
+  p.n_split = nc;
+  p.tiles_a = (long)ceil_div(M, kTiles[kWide].bm) * (nc / kTiles[kWide].bn);
+  p.grid = p.tiles_a + (long)ceil_div(M, kTiles[kNarrow].bm) * ceil_div(N - nc, kTiles[kNarrow].bn);
+  return p;
+}
+
+#ifdef FG_TESTING
+thread_local int t_forced_split = -1;   // test build: force the dense split at this column
+#endif
+
+// Picks the launch for a problem: the compiled shape with the smallest
+// estimated time, in CU cycles (tile_cycles per tile, tiles in rounds over the
+// CUs, which carries the wave-quantisation loss the zwzgs.cn DeepGEMM page
+// describes under "non-standard block sizes": a tile count just above a
+// multiple of the SM count leaves most of the last round idle; partial tiles
+// carry their padding), or for the dense layout the split onto two tile
+// shapes: the widest column range whose 256x256 tiles make whole rounds, the
+// remaining columns on 256x128 tiles. Contiguous tiles must not straddle an
+// aligned 128-row expert block. The fused SiLU-gate epilogue needs 256-column
+// tiles (one gate and one up block per row); bn256 restricts the choice to
+// those (and rules out the split).
+Plan pick_plan(int layout, int M, int N, int K, int G, int cus, bool bn256 = false) {
+  Plan best;
 #ifdef FG_TESTING
   const int forced = t_forced_tile;
-  if (forced >= 0)
-    return (!bn256 || kTiles[forced].bn == 256) && tile_allowed(layout, M, G, kTiles[forced]) ? forced : -1;
+  if (forced >= 0) {
+    if ((!bn256 || kTiles[forced].bn == 256) && tile_allowed(layout, M, G, kTiles[forced])) {
+      best.ti = forced;
+      best.grid = launch_grid(layout, M, N, G, kTiles[forced], cus);
+    }
+    return best;
+  }
+  if (t_forced_split >= 0) {
+    if (layout == FG_LAYOUT_DENSE && !bn256 && t_forced_split < N) best = split_plan(M, N, t_forced_split);
+    return best;
+  }
 #endif
-  int best = -1;
   double best_cost = 0.0;
   const double kblocks = K / 128;
   for (int i = 0; i < kNumTiles; ++i) {
@@ -125,12 +172,26 @@ int pick_tile(int layout, int M, int N, int K, int G, int cus, bool bn256 = fals
     if (bn256 && t.bn != 256) continue;
     const long tiles = count_tiles(layout, M, N, G, t);
     const long rounds = (tiles + cus - 1) / cus;
-    const double t_mfma = (double)t.bm * t.bn * 256.0 / (8192.0 * t.eff);
-    const double t_mem = (double)(t.bm + t.bn) * 128.0 / (t.waves >= 8 ? 30.0 : 24.0);
-    const double cost = (double)rounds * (kblocks * (t_mfma > t_mem ? t_mfma : t_mem) + kTileFixedCycles);
-    if (best < 0 || cost < best_cost * (1.0 - 1e-9)) {
-      best = i;
+    const double cost = (double)rounds * tile_cycles(t, kblocks);
+    if (best.ti < 0 || cost < best_cost * (1.0 - 1e-9)) {
+      best.ti = i;
+      best.grid = launch_grid(layout, M, N, G, t, cus);
       best_cost = cost;
+    }
+  }
+  if (layout == FG_LAYOUT_DENSE && !bn256) {
+    const Tile& w = kTiles[kWide];
+    const long tm = ceil_div(M, w.bm);
+    for (long nc = (N / w.bn) * w.bn; nc >= w.bn; nc -= w.bn) {
+      const long a = tm * (nc / w.bn);
+      if (a % cus) continue;
+      if (nc == N) break;   // whole rounds on the wide tile alone
+      const Plan sp = split_plan(M, N, (int)nc);
+      const long b = sp.grid - sp.tiles_a;
+      const double cost = (double)(a / cus) * tile_cycles(w, kblocks) +
+                          (double)((b + cus - 1) / cus) * tile_cycles(kTiles[kNarrow], kblocks);
+      if (cost < best_cost * (1.0 - 1e-9)) best = sp;
+      break;
     }
   }
   return best;
@@ -185,9 +246,10 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   const int st = current_device(&cus);
   if (st != FG_OK) return st;
 
-  const int ti = pick_tile(layout, M, N, K, G, cus, fused != nullptr);
-  if (ti < 0) return FG_EINVAL;   // (test build) a forced tile this call cannot use
-  const Tile& t = kTiles[ti];
+  const Plan plan = pick_plan(layout, M, N, K, G, cus, fused != nullptr);
+  if (plan.ti < 0) return FG_EINVAL;   // (test build) a forced tile this call cannot use
+  const int ti = plan.split ? fg::tiles::kSplitTile : plan.ti;
+  const Tile& t = kTiles[plan.ti];
   Params p;
   p.A = static_cast<const uint8_t*>(A);
   p.sa = sa;
@@ -206,9 +268,10 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   p.KB = K / 128;
   p.tiles_m = ceil_div(M, t.bm);   // the contiguous 256-row kernel counts its own
   p.tiles_n = ceil_div(N, t.bn);
-  const long tiles = launch_grid(layout, M, N, p.G, t, cus);
-  if (tiles > 0x7fffffffL) return FG_EINVAL;
-  const int grid = (int)tiles;
+  p.n_split = plan.n_split;
+  p.tiles_a = (int)plan.tiles_a;
+  if (plan.grid > 0x7fffffffL) return FG_EINVAL;
+  const int grid = (int)plan.grid;
 
   hipError_t e;
   if (fused)
@@ -228,9 +291,10 @@ int select_tile(int M, int N, int K, int G, int layout, int num_cus, int* ti, lo
   if (M < 0 || N < 0 || K < 0 || (layout != FG_LAYOUT_DENSE && G < 1)) return FG_EINVAL;
   if (layout == FG_LAYOUT_DENSE) G = 1;
   const int cus = num_cus > 0 ? num_cus : kDefaultCUs;
-  *ti = pick_tile(layout, M, N, K, G, cus, fused);
-  if (*ti < 0) return FG_EINVAL;
-  *grid = launch_grid(layout, M, N, G, kTiles[*ti], cus);
+  const Plan plan = pick_plan(layout, M, N, K, G, cus, fused);
+  if (plan.ti < 0) return FG_EINVAL;
+  *ti = plan.ti;   // the split plan reports its wide tile
+  *grid = plan.grid;
   return FG_OK;
 }
 
@@ -335,6 +399,7 @@ int fg_select_grid(int M, int N, int K, int G, int layout, int num_cus, int* gri
 // thread's later calls, or restore the automatic choice with bm = bn = 0. A
 // call that cannot use the forced tile returns FG_EINVAL.
 int fgt_force_tile(int bm, int bn) {
+  t_forced_split = -1;
   if (bm == 0 && bn == 0) {
     t_forced_tile = -1;
     return FG_OK;
@@ -346,6 +411,17 @@ int fgt_force_tile(int bm, int bn) {
     }
   }
   return FG_EINVAL;
+}
+
+// Test build only: run this thread's later dense calls on the two-shape split
+// kernel with columns [0, n_split) on 256x256 tiles (n_split a positive
+// multiple of 256 below N; otherwise the call returns FG_EINVAL), or restore
+// the automatic choice with n_split = -1.
+int fgt_force_split(int n_split) {
+  if (n_split != -1 && (n_split <= 0 || n_split % 256)) return FG_EINVAL;
+  t_forced_tile = -1;
+  t_forced_split = n_split;
+  return FG_OK;
 }
 #endif
 

@@ -107,6 +107,9 @@ struct Params {
   int N, K, G;
   int KB;                 // K / 128
   int tiles_m, tiles_n;   // tile grid of one group
+  // dense on two tile shapes (fp8_bs_gemm_split): columns [0, n_split) on the
+  // wide tiles, tiles_a of them; the rest on the narrow tiles
+  int n_split, tiles_a;
   // kEpiSwigluQuant outputs (I = N / 2 columns): codes [rows][I] (masked
   // [G][M][I]), scales [I/128][rows] (masked [G][I/128][M]), and optionally
   // the fp32 activation [rows][I] (masked [G][M][I]; null: not written)
@@ -964,6 +967,27 @@ __device__ __forceinline__ int contiguous_run_tiles(const Params& p, int* blk, i
   return *s_count;
 }
 
+// Position of workgroup b among nwg: consecutive positions are placed on the
+// same XCD (workgroups are dealt round-robin to the XCDs).
+__device__ __forceinline__ int xcd_position(int b, int nwg) {
+  const int x = b % kXCDs, l = b / kXCDs;
+  const int per = nwg / kXCDs, rem = nwg % kXCDs;
+  return x * per + (x < rem ? x : rem) + l;
+}
+
+// Tile position -> (m-block, n-block) of a tiles_m x tiles_n grid, walked in
+// groups of kGroupM m-blocks so the tiles resident on one XCD share A rows and
+// B columns in its L2.
+__device__ __forceinline__ void raster(int tile, int tiles_m, int tiles_n, int& mb, int& nbk) {
+  const int span = kGroupM * tiles_n;
+  const int grp = tile / span;
+  const int first = grp * kGroupM;
+  const int gsz = min(kGroupM, tiles_m - first);
+  const int in = tile - grp * span;
+  mb = first + in % gsz;
+  nbk = in / gsz;
+}
+
 template <int LAYOUT, class T, bool POW2 = false, int EPI = kEpiBf16>
 __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   constexpr int BM = T::BM, BN = T::BN;
@@ -974,26 +998,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   lds_u8* const lds = (lds_u8*)smem;
   const int t = threadIdx.x;
 
-  // ---- workgroup -> tile position. Consecutive positions are placed on the
-  // same XCD (workgroups are dealt round-robin to the XCDs); tiles are walked
-  // in groups of kGroupM m-blocks so the tiles resident on one XCD share A
-  // rows and B columns in its L2.
-  int pos;
-  {
-    const int b = blockIdx.x, nwg = gridDim.x;
-    const int x = b % kXCDs, l = b / kXCDs;
-    const int per = nwg / kXCDs, rem = nwg % kXCDs;
-    pos = x * per + (x < rem ? x : rem) + l;
-  }
-  auto raster = [&](int tile, int tiles_m, int& mb, int& nbk) {
-    const int span = kGroupM * p.tiles_n;
-    const int grp = tile / span;
-    const int first = grp * kGroupM;
-    const int gsz = min(kGroupM, tiles_m - first);
-    const int in = tile - grp * span;
-    mb = first + in % gsz;
-    nbk = in / gsz;
-  };
+  const int pos = xcd_position(blockIdx.x, gridDim.x);
 
   if constexpr (RUNS) {
     int* list = (int*)(smem + T::LDS_BYTES);
@@ -1006,7 +1011,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
         block_barrier();
       }
       int mb, nbk;
-      raster(tile, ntm, mb, nbk);
+      raster(tile, ntm, p.tiles_n, mb, nbk);
       const int e = list[mb];
       gemm_tile<LAYOUT, T, POW2, EPI>(p, lds, e >> 16, (e & 0xffff) * 128, nbk * BN, p.M);
     }
@@ -1019,7 +1024,7 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
       tile -= g * per;
     }
     int mb, nbk;
-    raster(tile, p.tiles_m, mb, nbk);
+    raster(tile, p.tiles_m, p.tiles_n, mb, nbk);
     const int m0 = mb * BM, n0 = nbk * BN;
 
     int rows_valid = p.M;  // rows of this slab that have an output
@@ -1044,5 +1049,30 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
   }
 }
 
+
+// Dense layout on two tile shapes in one launch. A problem whose tile count on
+// the wide tile TA leaves a partial last round (the wave quantisation the
+// zwzgs.cn DeepGEMM page describes under "non-standard block sizes") puts
+// columns [0, n_split) on TA tiles -- tiles_a of them, whole rounds over the
+// CUs -- and the remaining columns on the narrower TB tiles, which fill the
+// last round. Workgroups [0, tiles_a) take TA tiles, the rest TB tiles; both
+// groups are XCD-grouped and rasterised like the single-shape kernel.
+template <class TA, class TB, bool POW2>
+__global__ __launch_bounds__(TA::THREADS) void fp8_bs_gemm_split(Params p) {
+  static_assert(TA::THREADS == TB::THREADS, "both tile shapes run with the same workgroup size");
+  constexpr int LDS = TA::LDS_BYTES > TB::LDS_BYTES ? TA::LDS_BYTES : TB::LDS_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+  lds_u8* const lds = (lds_u8*)smem;
+  const int b = blockIdx.x, na = p.tiles_a;
+  int mb, nbk;
+  if (b < na) {
+    raster(xcd_position(b, na), (p.M + TA::BM - 1) / TA::BM, p.n_split / TA::BN, mb, nbk);
+    gemm_tile<kDense, TA, POW2, kEpiBf16>(p, lds, 0, mb * TA::BM, nbk * TA::BN, p.M);
+  } else {
+    raster(xcd_position(b - na, gridDim.x - na), (p.M + TB::BM - 1) / TB::BM,
+           (p.N - p.n_split + TB::BN - 1) / TB::BN, mb, nbk);
+    gemm_tile<kDense, TB, POW2, kEpiBf16>(p, lds, 0, mb * TB::BM, p.n_split + nbk * TB::BN, p.M);
+  }
+}
 
 }  // namespace fg

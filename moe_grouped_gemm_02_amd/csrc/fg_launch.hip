@@ -35,6 +35,14 @@ hipError_t launch_layout(int tile, const Params& p, int grid, hipStream_t s) {
     case 4: return launch_tile<LAYOUT, POW2, EPI, Cfg4>(p, grid, s);
     case 5: return launch_tile<LAYOUT, POW2, EPI, Cfg5>(p, grid, s);
     case 6: return launch_tile<LAYOUT, POW2, EPI, Cfg6>(p, grid, s);
+    case kSplitTile:
+      if constexpr (LAYOUT == kDense && EPI == kEpiBf16) {
+        hipLaunchKernelGGL((fp8_bs_gemm_split<SplitWide, SplitNarrow, POW2>), dim3(grid),
+                           dim3(SplitWide::THREADS), 0, s, p);
+        return hipGetLastError();
+      } else {
+        return hipErrorInvalidValue;
+      }
     default: return hipErrorInvalidValue;
   }
 }

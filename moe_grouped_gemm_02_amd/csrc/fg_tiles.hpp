@@ -18,6 +18,12 @@ using Cfg3 = TileCfg<128, 128, 2, 2, 4, false, 3, false, 3>;
 using Cfg4 = TileCfg<64, 112, 4, 1, 4, true, 3, true, 3, 4>;     // skinny M, HBM-bound
 using Cfg5 = TileCfg<256, 112, 4, 1, 3, true, 2, false, 3>;    // masked decode, HBM-bound
 using Cfg6 = TileCfg<256, 224, 4, 2, 2, true, 2, false, 3>;    // N = 7168: 32 column tiles
+// Dense problems whose wide-tile count leaves a partial last round: whole
+// rounds of 256x256 tiles, the remaining columns on 256x128 tiles
+// (fp8_bs_gemm_split); launched as tile index kSplitTile
+using SplitWide = Cfg0;
+using SplitNarrow = Cfg1;
+constexpr int kSplitTile = 7;
 }  // namespace tiles
 
 // Launches tile configuration `tile` (the index of its Cfg above) with `grid`

@@ -11,6 +11,14 @@ import workloads
 
 SENTINEL = 0x7E7E          # bf16 bits of a finite value no GEMM here produces by chance
 
+# Whole-output parity results of the full-size tests, printed in pytest's
+# terminal summary (tests/conftest.py) so that a quiet run still shows them.
+PARITY = []
+
+
+def record_parity(name, n_checked, max_ratio, frob, extra=""):
+    PARITY.append(f"{name}: n_checked={n_checked} max_ratio={max_ratio:.3f} frob={frob:.3e}{extra}")
+
 
 def dev():
     if not torch.cuda.is_available():

@@ -7,6 +7,7 @@ build also links libfg_testing.so: the same kernel objects, with host code
 built with FG_TESTING, which adds
 
     int fgt_force_tile(int bm, int bn);   /* per calling thread; 0, 0 = automatic */
+    int fgt_force_split(int n_split);     /* dense on the two-shape kernel; -1 = automatic */
 
 ``forced_tile(bm, bn)`` routes the package's calls through that library for the
 duration of a ``with`` block (on this thread's override) and restores the
@@ -28,6 +29,8 @@ def testing_lib():
         L = fg.load(TESTING_LIB_PATH)
         L.fgt_force_tile.argtypes = [ctypes.c_int, ctypes.c_int]
         L.fgt_force_tile.restype = ctypes.c_int
+        L.fgt_force_split.argtypes = [ctypes.c_int]
+        L.fgt_force_split.restype = ctypes.c_int
         _tlib = L
     return _tlib
 
@@ -48,3 +51,20 @@ def forced_tile(bm, bn):
     finally:
         fg._lib = saved
         L.fgt_force_tile(0, 0)
+
+
+@contextlib.contextmanager
+def forced_split(n_split):
+    """Run the package's dense calls inside the block on the two-shape kernel:
+    columns [0, n_split) on 256x256 tiles, the rest on 256x128 tiles."""
+    L = testing_lib()
+    saved = fg.lib()
+    rc = L.fgt_force_split(n_split)
+    if rc != 0:
+        raise fg.FGError(f"fgt_force_split({n_split}): {fg.strerror(rc)}")
+    fg._lib = L
+    try:
+        yield
+    finally:
+        fg._lib = saved
+        L.fgt_force_split(-1)

@@ -8,7 +8,7 @@ import re
 import pytest
 
 import moe_grouped_gemm_02_amd as fg
-from fgtesting import forced_tile as forced, testing_lib
+from fgtesting import forced_split, forced_tile as forced, testing_lib as _testing_lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fg.h")
@@ -170,6 +170,10 @@ def test_select_config_fills_the_machine():
             blocks = -(-M // 128)
             most = min(blocks, (blocks + G + 1) // 2) * -(-N // bn)
             assert grid == min(most, 256)
+        elif (layout, M, N) == (0, 8192, 7168):
+            # 3.5 rounds of 256x256 tiles: the two-shape split (3 whole rounds
+            # of 256x256 plus one round of 256x128)
+            assert (bm, bn) == (256, 256) and grid == 768 + 256
         else:
             assert grid == tiles
         if layout == 1:
@@ -187,6 +191,22 @@ def test_select_config_picks_the_measured_best_tiles():
     assert fg.select_config(9472, 4096, 7168, 8, 1) == (256, 224)
     assert fg.select_config(256, 7168, 2048, 16, 2) in ((256, 224), (256, 256))
     assert fg.select_config(8192, 7168, 18432, 1, 0) in ((256, 128), (256, 256), (256, 224))
+
+
+def test_dense_split_chosen_for_partial_rounds():
+    """The large dense FFN shape (32 x 28 tiles of 256x256 = 3.5 rounds over
+    256 CUs) runs on the two-shape kernel: 24 column tiles of 256x256 (3 whole
+    rounds) and the remaining 1024 columns as one round of 256x128 tiles. The
+    wide tile is the one reported; the grid counts both shapes."""
+    assert fg.select_config(8192, 7168, 18432, 1, 0) == (256, 256)
+    assert fg.select_grid(8192, 7168, 18432, 1, 0) == 768 + 256
+    # a problem already in whole rounds keeps the single shape
+    assert fg.select_grid(8192, 4096, 7168, 1, 0) == 512
+    # not for the fused epilogue (256-column tiles only) or the grouped layouts
+    assert fg.select_grid(8192, 7168, 18432, 1, fg.SELECT_SWIGLU_QUANT) == 32 * 28
+    with pytest.raises(fg.FGError):
+        with forced_split(100):
+            pass
 
 
 def test_select_config_rejects_bad_layout():
@@ -217,7 +237,7 @@ def test_testing_override_is_per_thread():
     seen = {}
 
     def other():
-        seen["other"] = testing_lib().fg_select_config(8192, 7168, 18432, 1, 0, 0, ctypes.byref(bm), None), bm.value
+        seen["other"] = _testing_lib().fg_select_config(8192, 7168, 18432, 1, 0, 0, ctypes.byref(bm), None), bm.value
 
     bm = ctypes.c_int()
     with forced(128, 128):

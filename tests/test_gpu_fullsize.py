@@ -12,7 +12,7 @@ import torch
 import oracle
 import moe_grouped_gemm_02_amd as fg
 from fgtest import (SENTINEL, d_bits, dense_inputs, fullsize_contiguous, fullsize_contiguous_ref,
-                    fullsize_quantized, masked_inputs, new_out, to_dev)
+                    fullsize_quantized, masked_inputs, new_out, record_parity, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +28,8 @@ def report(name, r):
     print(f"{name}: n_checked={r['n_checked']} max_ratio={r['max_ratio']:.4f} "
           f"frob={r['frob']:.4e} (bf16 floor {r['floor']:.4e}) n_bad={r['n_bad']} "
           f"untouched={r['untouched_ok']}", flush=True)
+    record_parity(name, r["n_checked"], r["max_ratio"], r["frob"],
+                  "" if r["untouched_ok"] else " ROWS WITHOUT OUTPUT WRITTEN")
 
 
 @POW2
@@ -46,7 +48,7 @@ def test_fullsize_dense(name, pow2):
     assert_all_finite(bits)
     ref = oracle.ref_dense(A, sa, B, sb)
     r = oracle.check(bits, ref)
-    report(name, r)
+    report(f"{name} {'pow2' if pow2 else 'fp32'}", r)
     assert r["ok"] and r["n_checked"] == M * N, r
 
 
@@ -63,7 +65,7 @@ def test_fullsize_contiguous(pow2):
     ref, valid = fullsize_contiguous_ref(pow2)
     assert_all_finite(bits[valid])
     r = oracle.check(bits, ref, valid, prefill_bits=SENTINEL)
-    report("contiguous", r)
+    report(f"contiguous {'pow2' if pow2 else 'fp32'}", r)
     assert r["ok"] and r["n_checked"] == int(valid.sum()) * N, r
 
 
@@ -81,5 +83,5 @@ def test_fullsize_masked(pow2):
     ref, valid = oracle.ref_masked(A, sa, B, sb, mm)
     assert_all_finite(bits[valid])
     r = oracle.check(bits, ref, valid, prefill_bits=SENTINEL)
-    report("masked", r)
+    report(f"masked {'pow2' if pow2 else 'fp32'}", r)
     assert r["ok"] and r["n_checked"] == int(valid.sum()) * N, r

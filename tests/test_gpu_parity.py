@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import moe_grouped_gemm_02_amd as fg
-from fgtesting import forced_tile as forced
+from fgtesting import forced_split, forced_tile as forced
 from fgtest import (SENTINEL, d_bits, dense_inputs, dev, make_contiguous, make_dense,
                     make_masked, masked_inputs, new_out, to_dev)
 
@@ -161,6 +161,20 @@ def test_every_tile_dense(forced_tile, K):
     print(f"tile {forced_tile} dense K={K}", flush=True)
     A, sa, B, sb = make_dense(300, 512, K, 60 + K)
     out = run_dense(A, sa, B, sb)
+    r = oracle.check(out, oracle.ref_dense(A, sa, B, sb))
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("M,N,n_split,K", [(300, 520, 256, 640), (300, 776, 512, 1152), (256, 384, 256, 128),
+                                           (64, 1000, 768, 256), (513, 264, 256, 384)])
+def test_dense_split_kernel(M, N, n_split, K):
+    """The dense two-shape kernel: columns [0, n_split) on 256x256 tiles, the
+    rest (ragged N, N % 128 != 0 included) on 256x128 tiles, ragged M, K from
+    one K-block to more than the deepest ring."""
+    print(f"dense split M={M} N={N} n_split={n_split} K={K}", flush=True)
+    A, sa, B, sb = make_dense(M, N, K, 63 + M + N)
+    with forced_split(n_split):
+        out = run_dense(A, sa, B, sb)
     r = oracle.check(out, oracle.ref_dense(A, sa, B, sb))
     assert r["ok"], r
 

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import moe_grouped_gemm_02_amd as fg
-from fgtesting import forced_tile as forced
+from fgtesting import forced_split, forced_tile as forced
 from fgtest import (SENTINEL, d_bits, dense_inputs, make_contiguous, make_dense, make_masked,
                     masked_inputs, new_out, quant_inputs, to_dev)
 
@@ -174,6 +174,20 @@ def test_dense_pow2_agrees_with_the_promotion_path():
 def test_dense_pow2_deterministic():
     A, sa, B, sb = make_dense(300, 512, 768, 136, pow2=True)
     assert np.array_equal(run_dense(A, sa, B, sb), run_dense(A, sa, B, sb))
+
+
+@pytest.mark.parametrize("M,N,n_split,K", [(300, 776, 512, 1152), (513, 264, 256, 128)])
+def test_dense_split_kernel_pow2(M, N, n_split, K):
+    """The dense two-shape kernel with power-of-two scales on the matrix core."""
+    print(f"pow2 dense split M={M} N={N} n_split={n_split} K={K}", flush=True)
+    A, sa, B, sb = make_dense(M, N, K, 64 + M, pow2=True)
+    Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
+    D = new_out((M, N))
+    with forced_split(n_split):
+        fg.gemm_fp8_nt_pow2(Ad, sad, Bd, sbd, D)
+    torch.cuda.synchronize()
+    r = oracle.check(d_bits(D), oracle.ref_dense(A, sa, B, sb))
+    assert r["ok"], r
 
 
 @pytest.mark.parametrize("forced_tile", TILES, indirect=True, ids=lambda t: f"{t[0]}x{t[1]}")

@@ -24,7 +24,7 @@ import oracle
 import moe_grouped_gemm_02_amd as fg
 from fgtesting import forced_tile as forced
 from fgtest import (fullsize_contiguous, fullsize_contiguous_ref, fullsize_quantized, make_contiguous, make_dense,
-                    make_masked, to_dev)
+                    make_masked, record_parity, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -179,6 +179,8 @@ def test_fullsize_masked_swiglu_quant(pow2):
             assert np.array_equal(codes, Qh[g][v]) and np.array_equal(scales, sqh[g].T[v])
     r = check_f32(acth[valid], oracle.swiglu_blocks(ref[valid]))
     print(f"masked act: n_checked={int(valid.sum()) * I} {r}", flush=True)
+    record_parity(f"fused masked act {'pow2' if pow2 else 'fp32'}", int(valid.sum()) * I, r["worst"], r["frob"],
+                  " (codes + scales bit-exact)")
     assert r["ok"], r
 
 
@@ -207,4 +209,6 @@ def test_fullsize_contiguous_swiglu_quant(pow2):
     assert np.array_equal(valid, valid_ref)
     r = check_f32(acth[valid], oracle.swiglu_blocks(ref[valid]))
     print(f"contiguous act: n_checked={int(valid.sum()) * I} {r}", flush=True)
+    record_parity(f"fused contiguous act {'pow2' if pow2 else 'fp32'}", int(valid.sum()) * I, r["worst"], r["frob"],
+                  " (codes + scales bit-exact)")
     assert r["ok"], r
