@@ -114,6 +114,7 @@ double tile_cycles(const Tile& t, double kblocks) {
 struct Plan {
   int ti = -1;
   bool split = false;
+  bool runs = false;   // contiguous: fp8_bs_gemm_runs (RunsFull + RunsHalf tiles)
   int n_split = 0;
   long tiles_a = 0;
   long grid = 0;
@@ -121,6 +122,36 @@ struct Plan {
 constexpr int kWide = 0, kNarrow = 1;   // kTiles indices of SplitWide / SplitNarrow
 static_assert(SplitWide::BM == 256 && SplitWide::BN == 256 && SplitNarrow::BM == 256 && SplitNarrow::BN == 128,
               "kTiles[kWide] / kTiles[kNarrow] describe the split kernel's tile shapes");
+constexpr int kRunsFull = 0, kRunsHalf = 2;   // kTiles indices of RunsFull / RunsHalf
+static_assert(RunsFull::BM == 256 && RunsFull::BN == 256 && RunsHalf::BM == 128 && RunsHalf::BN == 256,
+              "kTiles[kRunsFull] / kTiles[kRunsHalf] describe the runs kernel's tile shapes");
+
+// The contiguous runs kernel: one workgroup per CU at most (the workgroups
+// walk the work items), and no more than there can be 128-row items.
+Plan runs_plan(int M, int N, int cus) {
+  Plan p;
+  p.runs = true;
+  p.ti = kRunsFull;
+  const long most = (long)ceil_div(M, 128) * ceil_div(N, kTiles[kRunsFull].bn);
+  p.grid = most < cus ? most : cus;
+  return p;
+}
+
+// Estimated cycles of the runs kernel. The tile list depends on m_indices
+// (device memory), so the host takes the expected shape: G runs (one per
+// expert, at most one per block), half of them odd, i.e. S = runs / 2
+// single-block tiles and F = (blocks - S) / 2 two-block tiles per column; the
+// kernel's own rule then decides how the two-block tiles' last round runs.
+double runs_cycles(int M, int N, int G, int grid, double kblocks) {
+  const long nblk = ceil_div(M, 128);
+  const long runs = G < nblk ? G : nblk;
+  const long S = runs / 2, F = (nblk - S) / 2;
+  const long tn = ceil_div(N, kTiles[kRunsFull].bn);
+  const double tf = tile_cycles(kTiles[kRunsFull], kblocks), th = tile_cycles(kTiles[kRunsHalf], kblocks);
+  const long full_items = F * tn, rounds = full_items / grid, rest = full_items - rounds * grid;
+  if (rest && 2 * rest + S * tn <= grid) return (double)rounds * tf + th;
+  return (double)((full_items + grid - 1) / grid) * tf + (double)((S * tn + grid - 1) / grid) * th;
+}
 
 // The dense split for columns [0, nc) on wide tiles and [nc, N) on narrow ones.
 Plan split_plan(int M, int N, int nc) {
@@ -135,6 +166,7 @@ Plan split_plan(int M, int N, int nc) {
 
 #ifdef FG_TESTING
 thread_local int t_forced_split = -1;   // test build: force the dense split at this column
+thread_local bool t_forced_runs = false;   // test build: force the contiguous runs kernel
 #endif
 
 // Picks the launch for a problem: the compiled shape with the smallest
@@ -163,6 +195,10 @@ Plan pick_plan(int layout, int M, int N, int K, int G, int cus, bool bn256 = fal
     if (layout == FG_LAYOUT_DENSE && !bn256 && t_forced_split < N) best = split_plan(M, N, t_forced_split);
     return best;
   }
+  if (t_forced_runs) {
+    if (layout == FG_LAYOUT_CONTIGUOUS && tile_allowed(layout, M, G, kTiles[kRunsFull])) best = runs_plan(M, N, cus);
+    return best;
+  }
 #endif
   double best_cost = 0.0;
   const double kblocks = K / 128;
@@ -176,6 +212,14 @@ Plan pick_plan(int layout, int M, int N, int K, int G, int cus, bool bn256 = fal
     if (best.ti < 0 || cost < best_cost * (1.0 - 1e-9)) {
       best.ti = i;
       best.grid = launch_grid(layout, M, N, G, t, cus);
+      best_cost = cost;
+    }
+  }
+  if (layout == FG_LAYOUT_CONTIGUOUS && tile_allowed(layout, M, G, kTiles[kRunsFull])) {
+    const Plan rp = runs_plan(M, N, cus);
+    const double cost = runs_cycles(M, N, G, (int)rp.grid, kblocks);
+    if (cost < best_cost * (1.0 - 1e-9)) {
+      best = rp;
       best_cost = cost;
     }
   }
@@ -248,7 +292,7 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
 
   const Plan plan = pick_plan(layout, M, N, K, G, cus, fused != nullptr);
   if (plan.ti < 0) return FG_EINVAL;   // (test build) a forced tile this call cannot use
-  const int ti = plan.split ? fg::tiles::kSplitTile : plan.ti;
+  const int ti = plan.split ? fg::tiles::kSplitTile : plan.runs ? fg::tiles::kRunsTile : plan.ti;
   const Tile& t = kTiles[plan.ti];
   Params p;
   p.A = static_cast<const uint8_t*>(A);
@@ -266,7 +310,7 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   p.K = K;
   p.G = layout == FG_LAYOUT_DENSE ? 1 : G;
   p.KB = K / 128;
-  p.tiles_m = ceil_div(M, t.bm);   // the contiguous 256-row kernel counts its own
+  p.tiles_m = ceil_div(M, t.bm);   // the contiguous run-following kernels count their own
   p.tiles_n = ceil_div(N, t.bn);
   p.n_split = plan.n_split;
   p.tiles_a = (int)plan.tiles_a;
@@ -400,6 +444,7 @@ int fg_select_grid(int M, int N, int K, int G, int layout, int num_cus, int* gri
 // call that cannot use the forced tile returns FG_EINVAL.
 int fgt_force_tile(int bm, int bn) {
   t_forced_split = -1;
+  t_forced_runs = false;
   if (bm == 0 && bn == 0) {
     t_forced_tile = -1;
     return FG_OK;
@@ -420,7 +465,18 @@ int fgt_force_tile(int bm, int bn) {
 int fgt_force_split(int n_split) {
   if (n_split != -1 && (n_split <= 0 || n_split % 256)) return FG_EINVAL;
   t_forced_tile = -1;
+  t_forced_runs = false;
   t_forced_split = n_split;
+  return FG_OK;
+}
+
+// Test build only: run this thread's later contiguous calls on the runs
+// kernel (256x256 run-following tiles, 128x256 single-block and tail tiles)
+// whenever its tile list fits, or restore the automatic choice with on = 0.
+int fgt_force_runs(int on) {
+  t_forced_tile = -1;
+  t_forced_split = -1;
+  t_forced_runs = on != 0;
   return FG_OK;
 }
 #endif

@@ -917,11 +917,15 @@ constexpr bool run_tiles() {
 // among its rows, -1 if it has none, the rule the 128-row tiles use -- into
 // blk[]. Pass 2 (wave 0, 64 blocks at a time, one lane each): a block starts
 // a run when its expert differs from the previous block's, and starts a tile
-// when it lies an even number of blocks after its run's start. Entry i of
-// list[] is (block | expert << 16) of the i-th tile in row order. Returns the
-// number of tiles; every thread of the workgroup must call it.
-template <int THREADS>
-__device__ __forceinline__ int contiguous_run_tiles(const Params& p, int* blk, int* list, int* s_count) {
+// when it lies an even number of blocks after its run's start. Entries are
+// (block | expert << 16) in row order. Without SINGLES every tile goes to
+// list[0 ..) and s_count[0] is their number. With SINGLES the last tile of a
+// run with an odd number of blocks (it covers a single block of the run) goes
+// to the back, list[kRunMaxBlocks - 1], list[kRunMaxBlocks - 2], ..., the
+// two-block tiles to the front; s_count[0] / s_count[1] are their numbers.
+// Every thread of the workgroup must call it.
+template <int THREADS, bool SINGLES>
+__device__ __forceinline__ void contiguous_run_tiles(const Params& p, int* blk, int* list, int* s_count) {
   const int t = threadIdx.x, lane = t & 63;
   const int nblk = (p.M + 127) / 128;
   constexpr int BPI = THREADS / 32;   // blocks per pass-1 iteration
@@ -945,7 +949,7 @@ __device__ __forceinline__ int contiguous_run_tiles(const Params& p, int* blk, i
   }
   __syncthreads();
   if (t < 64) {
-    int prev_e = -1, prev_rs = 0, count = 0;
+    int prev_e = -1, prev_rs = 0, count = 0, singles = 0;
     const unsigned long long lt = (1ull << lane) - 1ull, le = lt | (1ull << lane);
     for (int c0 = 0; c0 < nblk; c0 += 64) {
       const int bk = c0 + lane;
@@ -955,16 +959,23 @@ __device__ __forceinline__ int contiguous_run_tiles(const Params& p, int* blk, i
       const unsigned long long starts = __ballot(e >= 0 && e != before) & le;
       const int rs = starts ? c0 + 63 - __clzll((long long)starts) : prev_rs;   // start of this block's run
       const bool first = e >= 0 && ((bk - rs) & 1) == 0;
-      const unsigned long long firsts = __ballot(first);
-      if (first) list[count + __popcll(firsts & lt)] = bk | (e << 16);
-      count += __popcll(firsts);
+      // the tile's second block is outside the run: a single-block tile
+      const bool single = SINGLES && first && (bk + 1 >= nblk || blk[bk + 1] != e);
+      const unsigned long long fulls = __ballot(first && !single);
+      const unsigned long long ones = __ballot(single);
+      if (first && !single) list[count + __popcll(fulls & lt)] = bk | (e << 16);
+      if (single) list[kRunMaxBlocks - 1 - (singles + __popcll(ones & lt))] = bk | (e << 16);
+      count += __popcll(fulls);
+      singles += __popcll(ones);
       prev_e = __shfl(e, 63);
       prev_rs = __shfl(rs, 63);
     }
-    if (t == 0) *s_count = count;
+    if (t == 0) {
+      s_count[0] = count;
+      if (SINGLES) s_count[1] = singles;
+    }
   }
   __syncthreads();
-  return *s_count;
 }
 
 // Position of workgroup b among nwg: consecutive positions are placed on the
@@ -1002,7 +1013,8 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
 
   if constexpr (RUNS) {
     int* list = (int*)(smem + T::LDS_BYTES);
-    const int ntm = contiguous_run_tiles<T::THREADS>(p, (int*)smem, list, &s_group);
+    contiguous_run_tiles<T::THREADS, false>(p, (int*)smem, list, &s_group);
+    const int ntm = s_group;
     const int total = ntm * p.tiles_n;
     for (int tile = pos; tile < total; tile += gridDim.x) {
       if (tile != pos) {   // the previous tile's epilogue is done with LDS
@@ -1072,6 +1084,68 @@ __global__ __launch_bounds__(TA::THREADS) void fp8_bs_gemm_split(Params p) {
     raster(xcd_position(b - na, gridDim.x - na), (p.M + TB::BM - 1) / TB::BM,
            (p.N - p.n_split + TB::BN - 1) / TB::BN, mb, nbk);
     gemm_tile<kDense, TB, POW2, kEpiBf16>(p, lds, 0, mb * TB::BM, p.n_split + nbk * TB::BN, p.M);
+  }
+}
+
+// Contiguous layout on run-following 256-row tiles (TF, 256 x BN) with the
+// work the 256-row tiles would waste put on 128-row tiles (TH, 128 x BN):
+//  * the last tile of a run with an odd number of 128-row blocks covers one
+//    block of the run, so it runs as a 128-row tile (the 256-row kernel
+//    computes another expert's block, or padding, beside it and discards it);
+//  * the two-block tiles fill whole rounds over the workgroups; if the rest
+//    of them, split into 128-row halves, fits one round together with the
+//    single-block tiles, it runs that way (the wave-quantisation tail the
+//    zwzgs.cn DeepGEMM page describes under "non-standard block sizes"),
+//    otherwise every two-block tile runs whole.
+// The workgroups walk the work items persistently: two-block tiles first,
+// then the 128-row items. The tile list comes from m_indices (device memory),
+// so every workgroup derives it and the split itself.
+template <class TF, class TH, bool POW2, int EPI>
+__global__ __launch_bounds__(TF::THREADS) void fp8_bs_gemm_runs(Params p) {
+  static_assert(TF::BM == 256 && TH::BM == 128 && TF::BN == TH::BN && TF::THREADS == TH::THREADS,
+                "two-block tiles of 256 rows, single-block tiles of 128 rows, same columns and workgroup");
+  constexpr int LDS = TF::LDS_BYTES > TH::LDS_BYTES ? TF::LDS_BYTES : TH::LDS_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS + kRunMaxBlocks * 4];
+  __shared__ int s_count[2];
+  lds_u8* const lds = (lds_u8*)smem;
+  int* list = (int*)(smem + LDS);
+  contiguous_run_tiles<TF::THREADS, true>(p, (int*)smem, list, s_count);
+  const int F = s_count[0], S = s_count[1], tn = p.tiles_n;
+  const long grid = gridDim.x;
+  const long full_items = (long)F * tn;
+  long whole = full_items;   // two-block tiles that run as 256-row tiles
+  {
+    const long rounds = full_items / grid, rest = full_items - rounds * grid;
+    if (rest && 2 * rest + (long)S * tn <= grid) whole = rounds * grid;
+  }
+  const long halves = 2 * (full_items - whole);
+  const long items = whole + halves + (long)S * tn;
+  const long pos = xcd_position(blockIdx.x, gridDim.x);
+  for (long w = pos; w < items; w += grid) {
+    if (w != pos) {   // the previous tile's epilogue is done with LDS
+      wait_vm<0>();
+      wait_lgkm0();
+      block_barrier();
+    }
+    int mb, nbk;
+    if (w < whole) {
+      raster((int)w, F, tn, mb, nbk);
+      const int e = list[mb];
+      gemm_tile<kContiguous, TF, POW2, EPI>(p, lds, e >> 16, (e & 0xffff) * 128, nbk * TF::BN, p.M);
+    } else {
+      const long h = w - whole;
+      int e, m0;
+      if (h < halves) {   // one 128-row half of a two-block tile
+        raster((int)(whole + h / 2), F, tn, mb, nbk);
+        e = list[mb];
+        m0 = (e & 0xffff) * 128 + (int)(h & 1) * 128;
+      } else {            // a single-block tile
+        raster((int)(h - halves), S, tn, mb, nbk);
+        e = list[kRunMaxBlocks - 1 - mb];
+        m0 = (e & 0xffff) * 128;
+      }
+      gemm_tile<kContiguous, TH, POW2, EPI>(p, lds, e >> 16, m0, nbk * TH::BN, p.M);
+    }
   }
 }
 

@@ -43,6 +43,14 @@ hipError_t launch_layout(int tile, const Params& p, int grid, hipStream_t s) {
       } else {
         return hipErrorInvalidValue;
       }
+    case kRunsTile:
+      if constexpr (LAYOUT == kContiguous) {
+        hipLaunchKernelGGL((fp8_bs_gemm_runs<RunsFull, RunsHalf, POW2, EPI>), dim3(grid),
+                           dim3(RunsFull::THREADS), 0, s, p);
+        return hipGetLastError();
+      } else {
+        return hipErrorInvalidValue;
+      }
     default: return hipErrorInvalidValue;
   }
 }

@@ -24,6 +24,11 @@ using Cfg6 = TileCfg<256, 224, 4, 2, 2, true, 2, false, 3>;    // N = 7168: 32 c
 using SplitWide = Cfg0;
 using SplitNarrow = Cfg1;
 constexpr int kSplitTile = 7;
+// Contiguous layout: run-following 256x256 tiles with the single-block and
+// tail work on 128x256 tiles (fp8_bs_gemm_runs); launched as tile index kRunsTile
+using RunsFull = Cfg0;
+using RunsHalf = Cfg2;
+constexpr int kRunsTile = 8;
 }  // namespace tiles
 
 // Launches tile configuration `tile` (the index of its Cfg above) with `grid`

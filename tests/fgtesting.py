@@ -8,6 +8,7 @@ built with FG_TESTING, which adds
 
     int fgt_force_tile(int bm, int bn);   /* per calling thread; 0, 0 = automatic */
     int fgt_force_split(int n_split);     /* dense on the two-shape kernel; -1 = automatic */
+    int fgt_force_runs(int on);           /* contiguous on the runs kernel; 0 = automatic */
 
 ``forced_tile(bm, bn)`` routes the package's calls through that library for the
 duration of a ``with`` block (on this thread's override) and restores the
@@ -31,6 +32,8 @@ def testing_lib():
         L.fgt_force_tile.restype = ctypes.c_int
         L.fgt_force_split.argtypes = [ctypes.c_int]
         L.fgt_force_split.restype = ctypes.c_int
+        L.fgt_force_runs.argtypes = [ctypes.c_int]
+        L.fgt_force_runs.restype = ctypes.c_int
         _tlib = L
     return _tlib
 
@@ -68,3 +71,18 @@ def forced_split(n_split):
     finally:
         fg._lib = saved
         L.fgt_force_split(-1)
+
+
+@contextlib.contextmanager
+def forced_runs():
+    """Run the package's contiguous calls inside the block on the runs kernel
+    (256x256 run-following tiles, 128x256 single-block and tail tiles)."""
+    L = testing_lib()
+    saved = fg.lib()
+    L.fgt_force_runs(1)
+    fg._lib = L
+    try:
+        yield
+    finally:
+        fg._lib = saved
+        L.fgt_force_runs(0)

@@ -185,10 +185,11 @@ def test_select_config_picks_the_measured_best_tiles():
     # fastest on an MI355X when every compiled tile was forced in turn: the
     # smallest tile that gives 256 workgroups for M=256, the largest tiles for
     # the big dense and masked problems (fewer re-reads of A and B; 256x224
-    # splits N = 7168 into 32 whole column tiles), and the widest tile with
-    # BM | 128 for the contiguous layout.
+    # splits N = 7168 into 32 whole column tiles), and for the contiguous
+    # layout the runs kernel (256x256 run-following tiles, 128x256 tiles for
+    # single blocks and the last round).
     assert fg.select_config(256, 7168, 7168, 1, 0) == (64, 112)
-    assert fg.select_config(9472, 4096, 7168, 8, 1) == (256, 224)
+    assert fg.select_config(9472, 4096, 7168, 8, 1) == (256, 256)
     assert fg.select_config(256, 7168, 2048, 16, 2) in ((256, 224), (256, 256))
     assert fg.select_config(8192, 7168, 18432, 1, 0) in ((256, 128), (256, 256), (256, 224))
 

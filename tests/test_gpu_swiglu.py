@@ -22,7 +22,7 @@ import torch
 
 import oracle
 import moe_grouped_gemm_02_amd as fg
-from fgtesting import forced_tile as forced
+from fgtesting import forced_runs, forced_tile as forced
 from fgtest import (fullsize_contiguous, fullsize_contiguous_ref, fullsize_quantized, make_contiguous, make_dense,
                     make_masked, record_parity, to_dev)
 
@@ -37,6 +37,10 @@ SCALES = pytest.mark.parametrize("pow2", [False, True], ids=["fp32_scales", "pow
 def forced_tile(request):
     if request.param is None:
         yield None
+        return
+    if request.param == "runs":
+        with forced_runs():
+            yield "runs"
         return
     bm, bn = request.param
     with forced(bm, bn):
@@ -93,8 +97,8 @@ def test_dense_swiglu_quant(forced_tile, M, N, K, seed, pow2):
     check_rows(Q.cpu().numpy(), sq.cpu().numpy().T, act.cpu().numpy(), ref_act, np.ones(M, bool), pow2)
 
 
-@pytest.mark.parametrize("forced_tile", [None, (128, 256), (256, 256)], indirect=True,
-                         ids=lambda t: "auto" if t is None else f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("forced_tile", [None, (128, 256), (256, 256), "runs"], indirect=True,
+                         ids=lambda t: "auto" if t is None else t if isinstance(t, str) else f"{t[0]}x{t[1]}")
 @SCALES
 def test_contiguous_swiglu_quant(forced_tile, pow2):
     print(f"swiglu contiguous tile={forced_tile} pow2={pow2}", flush=True)
