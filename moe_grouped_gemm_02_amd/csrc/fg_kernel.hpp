@@ -462,10 +462,12 @@ __device__ __forceinline__ void swiglu_quant_epilogue(const Params& p, const f32
 }
 
 // One BM x BN output tile of expert g (dense: g = 0) whose first row is m0
-// and first column n0; rows_valid bounds the rows that have an output.
+// and first column n0; rows_valid bounds the rows that have an output. The
+// tile sums K-blocks [kb0, kb0 + nkb) (nkb = 0: all of them, K / 128).
 template <int LAYOUT, class T, bool POW2, int EPI>
 __device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, int g, const int m0,
-                                          const int n0, const int rows_valid) {
+                                          const int n0, const int rows_valid, const int kb0 = 0,
+                                          int nkb = 0) {
   constexpr int BM = T::BM, BN = T::BN, W = T::W, WM = T::WM, WN = T::WN;
   constexpr int TM = T::TM, TN = T::TN, PD = T::PD, R = T::RING;
   constexpr int PL = T::PL, P = T::PARTS;
@@ -481,6 +483,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, in
   g = uniform(g);
 
   const int K = p.K, KB = p.KB, M = p.M;
+  if (nkb == 0) nkb = KB;
   const uint8_t* Ag = p.A + (LAYOUT == kMasked ? (size_t)g * M * K : 0);
   const float* sag = p.sa + (LAYOUT == kMasked ? (size_t)g * KB * M : 0);
   const uint8_t* Bg = p.B + (LAYOUT != kDense ? (size_t)g * p.N * K : 0);
@@ -553,10 +556,10 @@ __device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, in
   };
   auto soff_of = [&](int ka, int kbb) {
     Soff o;
-    o.a = (uint32_t)ka * (uint32_t)kKBlock;
-    o.b = (uint32_t)kbb * (uint32_t)kKBlock;
+    o.a = (uint32_t)(kb0 + ka) * (uint32_t)kKBlock;
+    o.b = (uint32_t)(kb0 + kbb) * (uint32_t)kKBlock;
 #pragma unroll
-    for (int q = 0; q < T::SC_INSTR; ++q) o.sc[q] = (uint32_t)ka * sc_stride[q];
+    for (int q = 0; q < T::SC_INSTR; ++q) o.sc[q] = (uint32_t)(kb0 + ka) * sc_stride[q];
     return o;
   };
   constexpr int NA = T::A_INSTR, NSC = T::SC_INSTR, NB = T::B_INSTR;
@@ -647,14 +650,14 @@ __device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, in
   if constexpr (SPLIT) {
     static_for<2>([&](auto x_c) {
       constexpr int x = decltype(x_c)::value;
-      const Soff o = soff_of(min(x, KB - 1), min(x, KB - 1));
+      const Soff o = soff_of(min(x, nkb - 1), min(x, nkb - 1));
       static_for<D>([&](auto d_c) { issue(d_c, x_c, x_c, o); });
     });
   } else {
     static_for<SB>([&](auto x_c) {
       constexpr int x = decltype(x_c)::value;       // group g(x - SB)
       constexpr int ka = x - SB + SA;               // its A K-block (< 0: none)
-      const Soff o = soff_of(min(ka < 0 ? 0 : ka, KB - 1), min(x, KB - 1));
+      const Soff o = soff_of(min(ka < 0 ? 0 : ka, nkb - 1), min(x, nkb - 1));
       static_for<D>([&](auto d_c) {
         constexpr int d = decltype(d_c)::value;
         constexpr bool a_part = d < NA + NSC;
@@ -779,8 +782,8 @@ __device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, in
     using NxtA = std::integral_constant<int, NXA>;
     using CurB = std::integral_constant<int, CB>;
     using NxtB = std::integral_constant<int, NXB>;
-    const Soff head = soff_of(min(kb + SA, KB - 1), min(kb + SB, KB - 1));           // group g(kb)
-    const Soff tail = soff_of(min(kb - 1 + SA, KB - 1), min(kb - 1 + SB, KB - 1));   // group g(kb-1)
+    const Soff head = soff_of(min(kb + SA, nkb - 1), min(kb + SB, nkb - 1));           // group g(kb)
+    const Soff tail = soff_of(min(kb - 1 + SA, nkb - 1), min(kb - 1 + SB, nkb - 1));   // group g(kb-1)
     (void)tail;
     float sa_next[TM], sb_next0 = 0.f, sb_next1 = 0.f;
     static_for<STEPS>([&](auto u_c) {
@@ -829,7 +832,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, in
       step_fence();
     });
     set_scales(std::integral_constant<int, (PH + 1) & 1>{}, sa_next, sb_next0, sb_next1);
-    return ++kb == KB;
+    return ++kb == nkb;
   };
   bool done = false;
   for (;;) {
@@ -842,7 +845,7 @@ __device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, in
   // exit path per phase that did this work would keep the register allocator
   // from holding each accumulator in one register across the phases).
   if constexpr (!POW2) {
-    const int last = (KB - 1) % T::UNROLL;
+    const int last = (nkb - 1) % T::UNROLL;
     static_for<T::UNROLL>([&](auto ph_c) {
       constexpr int PH = decltype(ph_c)::value;
       if (last == PH) {
