@@ -38,7 +38,10 @@ milliseconds of sustained load to settle. Non-headline entries then time
 max(5, steps/10) launches. Each entry also gives `launch_us_median_min_max`
 from one event pair per launch (a separate pass), and `warm_kernel_us`: the
 same calls on a single input copy, resident in the MALL where it fits
-(reported beside the cold numbers, never as `value`).
+(reported beside the cold numbers, never as `value`). `mfma_ceiling` is what
+the matrix cores sustain on this device for the GEMM's inner loop with no
+memory traffic (random and all-zero E4M3 codes), and roofline
+`frac_of_measured_mfma_ceiling` the headline kernel against it.
 """
 import argparse
 import ctypes
@@ -378,6 +381,54 @@ def cpu_baseline(name, target_s):
                       f"host cpus {len(os.sched_getaffinity(0))}"}
 
 
+def mfma_ceiling(torch, warmup_ms):
+    """What the matrix cores sustain on this device for the GEMM's inner loop
+    with no memory traffic (libfg_ceiling.so, a helper built beside the
+    library): 8 waves per CU, each issuing its 64x128 tile's 32 E4M3 MFMAs per
+    K-block on fragments held in registers -- with the fp32-scale promotion (C
+    = 0, 4 FMAs per MFMA), with power-of-two accumulation, and with the
+    promotion on all-zero codes. Random codes draw the matrix cores' real
+    power; the gap to the zero-code figure is the power-limited clock."""
+    import numpy as np
+    L = ctypes.CDLL(os.path.join(ROOT, "moe_grouped_gemm_02_amd", "libfg_ceiling.so"))
+    L.fgc_src_words.restype = ctypes.c_int
+    L.fgc_flop_per_workgroup_iteration.restype = ctypes.c_double
+    L.fgc_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_void_p]
+    L.fgc_mfma_loop.restype = ctypes.c_int
+    n = L.fgc_src_words()
+    codes = np.random.default_rng(11).integers(0, 256, size=4 * n, dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] ^= 1          # finite codes only (no 0x7f / 0xff NaN)
+    src = torch.from_numpy(codes.view(np.int32).copy()).cuda()
+    zeros = torch.zeros_like(src)
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 2000
+    out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    flop = L.fgc_flop_per_workgroup_iteration() * iters * grid
+    res = {}
+    for name, mode, data in (("random_fp32_promotion", 0, src), ("random_pow2", 1, src),
+                             ("zeros_fp32_promotion", 0, zeros)):
+        def launch():
+            if L.fgc_mfma_loop(ctypes.c_void_p(data.data_ptr()), ctypes.c_void_p(out.data_ptr()), mode, grid,
+                               iters, stream) != 0:
+                raise RuntimeError("fgc_mfma_loop failed")
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < warmup_ms:
+            launch()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        tf = flop * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        res[name] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+    res["workgroups"] = grid
+    return res
+
+
 def kernel_source_hash():
     """Hash of what defines the kernels: the kernel template with comments and
     whitespace removed, and the tile-configuration lines that instantiate it.
@@ -573,6 +624,12 @@ def main():
     if args.calibrate_copy_mb:
         copy_calibration(args.calibrate_copy_mb, torch)
     roof["traffic"] = measured_traffic(args.workload) if not head_pow2 else None
+    ceiling = None
+    if full:
+        ceiling = mfma_ceiling(torch, args.warmup_ms)
+        if not hbm_bound:
+            key = "random_pow2" if head_pow2 else "random_fp32_promotion"
+            roof["frac_of_measured_mfma_ceiling"] = round(achieved_tflops / ceiling[key]["tflops"], 4)
 
     line = {
         "metric": "FP8 TFLOPS (dense + grouped MoE) and % of MI355X dense FP8 MFMA peak",
@@ -595,6 +652,7 @@ def main():
                    "out": "bf16", "tile": hs["tile"], "input_copies": hs["input_copies"],
                    "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2)},
         "roofline": roof,
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu_cfg.get(args.workload),
         "cpu_baseline_per_config": cpu_cfg or None,
         "per_workload": per,

@@ -6,6 +6,9 @@ tree; nothing is installed elsewhere. The GEMM kernels of each layout and scale
 kind are compiled as separate objects (fg_launch.hip with FG_LAUNCH_PART =
 2 * layout + pow2), in parallel, then linked with the host and quantiser code.
 
+libfg_ceiling.so (fg_ceiling.hip) is a benchmark helper that bench.py loads to
+measure the matrix cores' ceiling on this device; the library does not use it.
+
 A second library, libfg_testing.so, links the same kernel objects with the
 host code built with FG_TESTING: it adds a per-thread tile override
 (fgt_force_tile) that the test suite uses to run every compiled tile. The
@@ -21,10 +24,11 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfg.so")
 TESTING_LIB = os.path.join(HERE, "libfg_testing.so")
+CEILING_LIB = os.path.join(HERE, "libfg_ceiling.so")
 LAUNCH_PARTS = 6   # {dense, contiguous, masked} x {fp32 scales, power-of-two scales}
 # (object name, source, extra flags)
 UNITS = [("fg_host", "fg_host.hip", []), ("fg_host_testing", "fg_host.hip", ["-DFG_TESTING"]),
-         ("fg_quant", "fg_quant.hip", [])] + [
+         ("fg_quant", "fg_quant.hip", []), ("fg_ceiling", "fg_ceiling.hip", [])] + [
     (f"fg_launch_{i}", "fg_launch.hip", [f"-DFG_LAUNCH_PART={i}"]) for i in range(LAUNCH_PARTS)]
 HEADERS = ["fg_kernel.hpp", "fg_e4m3.hpp", "fg_tiles.hpp"]
 
@@ -70,9 +74,10 @@ def build(verbose=False, jobs=None):
         raise RuntimeError("hipcc failed building " + ", ".join(failed))
     host = os.path.join(OBJ, "fg_host.o")
     host_t = os.path.join(OBJ, "fg_host_testing.o")
-    common = [o for o in objs if o not in (host, host_t)]
-    for out, host_obj in ((LIB, host), (TESTING_LIB, host_t)):
-        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", host_obj, *common, "-o", out + ".tmp"]
+    ceiling = os.path.join(OBJ, "fg_ceiling.o")
+    common = [o for o in objs if o not in (host, host_t, ceiling)]
+    for out, link in ((LIB, [host, *common]), (TESTING_LIB, [host_t, *common]), (CEILING_LIB, [ceiling])):
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link, "-o", out + ".tmp"]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -262,3 +262,16 @@ def test_contiguous_256_row_tiles_only_within_the_tile_list():
             fg.select_config(2048 * 128 + 1, 4096, 7168, 8, 1)
         # dense and masked have no such limit
         assert fg.select_config(2048 * 128 + 1, 4096, 7168, 1, 0) == (256, 224)
+
+
+def test_ceiling_helper_loads():
+    """The benchmark helper bench.py loads to measure the matrix-core ceiling
+    (not part of the library) is built and exports its launcher."""
+    L = ctypes.CDLL(os.path.join(os.path.dirname(fg.LIB_PATH), "libfg_ceiling.so"), mode=os.RTLD_NOW)
+    for name in ("fgc_src_words", "fgc_flop_per_workgroup_iteration", "fgc_mfma_loop"):
+        assert hasattr(L, name), name
+    L.fgc_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_void_p]
+    assert L.fgc_mfma_loop(None, None, 0, 1, 1, None) == -1        # rejected before any launch
+    L.fgc_src_words.restype = ctypes.c_int
+    assert L.fgc_src_words() > 0
