@@ -63,7 +63,11 @@ enum {
                             8, misalignment,
                             G < 1 for a grouped call, unknown
                             layout or scale kind; N not a multiple
-                            of 256 for the fused calls */
+                            of 256 for the fused calls; an operand
+                            (M x K or N x K bytes, per expert) of
+                            2^31 bytes or more, or N > 4194296 (the
+                            kernels address these with 32-bit byte
+                            offsets) */
   FG_EUNSUPPORTED = -2,  /* current device is not gfx950 */
   FG_ELAUNCH = -3,       /* the kernel launch failed (hipGetLastError) */
   FG_EDEVICE = -4        /* a HIP runtime query failed */

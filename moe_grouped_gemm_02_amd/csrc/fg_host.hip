@@ -16,6 +16,9 @@ using fg::Params;
 
 // ---------------------------------------------------------------- devices
 constexpr int kMaxDevices = 64;
+// largest N (a multiple of 8) whose 256-row output tile, 256 x N bf16, stays
+// below 2^31 bytes
+constexpr int kMaxN = 4194296;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
 std::atomic<int> g_dev_cus[kMaxDevices];
 
@@ -110,13 +113,14 @@ double tile_cycles(const Tile& t, double kblocks) {
 
 // A launch plan: one compiled tile shape (index ti), or (split) the dense
 // two-shape kernel -- columns [0, n_split) on SplitWide tiles in whole rounds
-// (tiles_a of them), the rest on SplitNarrow tiles.
+// (tiles_a of them), the rest on SplitNarrow tiles (tiles_b), walked by at
+// most one workgroup per CU.
 struct Plan {
   int ti = -1;
   bool split = false;
   bool runs = false;   // contiguous: fp8_bs_gemm_runs (RunsFull + RunsHalf tiles)
   int n_split = 0;
-  long tiles_a = 0;
+  long tiles_a = 0, tiles_b = 0;
   long grid = 0;
 };
 constexpr int kWide = 0, kNarrow = 1;   // kTiles indices of SplitWide / SplitNarrow
@@ -154,13 +158,15 @@ double runs_cycles(int M, int N, int G, int grid, double kblocks) {
 }
 
 // The dense split for columns [0, nc) on wide tiles and [nc, N) on narrow ones.
-Plan split_plan(int M, int N, int nc) {
+Plan split_plan(int M, int N, int nc, int cus) {
   Plan p;
   p.split = true;
   p.ti = kWide;
   p.n_split = nc;
   p.tiles_a = (long)ceil_div(M, kTiles[kWide].bm) * (nc / kTiles[kWide].bn);
-  p.grid = p.tiles_a + (long)ceil_div(M, kTiles[kNarrow].bm) * ceil_div(N - nc, kTiles[kNarrow].bn);
+  p.tiles_b = (long)ceil_div(M, kTiles[kNarrow].bm) * ceil_div(N - nc, kTiles[kNarrow].bn);
+  const long most = p.tiles_a > p.tiles_b ? p.tiles_a : p.tiles_b;
+  p.grid = most < cus ? most : cus;
   return p;
 }
 
@@ -192,7 +198,7 @@ Plan pick_plan(int layout, int M, int N, int K, int G, int cus, bool bn256 = fal
     return best;
   }
   if (t_forced_split >= 0) {
-    if (layout == FG_LAYOUT_DENSE && !bn256 && t_forced_split < N) best = split_plan(M, N, t_forced_split);
+    if (layout == FG_LAYOUT_DENSE && !bn256 && t_forced_split < N) best = split_plan(M, N, t_forced_split, cus);
     return best;
   }
   if (t_forced_runs) {
@@ -230,8 +236,8 @@ Plan pick_plan(int layout, int M, int N, int K, int G, int cus, bool bn256 = fal
       const long a = tm * (nc / w.bn);
       if (a % cus) continue;
       if (nc == N) break;   // whole rounds on the wide tile alone
-      const Plan sp = split_plan(M, N, (int)nc);
-      const long b = sp.grid - sp.tiles_a;
+      const Plan sp = split_plan(M, N, (int)nc, cus);
+      const long b = sp.tiles_b;
       const double cost = (double)(a / cus) * tile_cycles(w, kblocks) +
                           (double)((b + cus - 1) / cus) * tile_cycles(kTiles[kNarrow], kblocks);
       if (cost < best_cost * (1.0 - 1e-9)) best = sp;
@@ -284,7 +290,9 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   if (m_indices && !aligned(m_indices, 4)) return FG_EINVAL;
   if (masked_m && !aligned(masked_m, 4)) return FG_EINVAL;
   // the kernels address one expert's A or B with 32-bit byte offsets
-  if ((long long)M * K > 0x7fffffffLL || (long long)N * K > 0x7fffffffLL) return FG_EINVAL;
+  // 32-bit byte offsets: operand rows (M x K, N x K per expert) and the output
+  // rows of one 256-row tile (256 x N bf16)
+  if ((long long)M * K > 0x7fffffffLL || (long long)N * K > 0x7fffffffLL || N > kMaxN) return FG_EINVAL;
 
   int cus = 0;
   const int st = current_device(&cus);
@@ -484,7 +492,7 @@ int fgt_force_runs(int on) {
 const char* fg_strerror(int code) {
   switch (code) {
     case FG_OK: return "success";
-    case FG_EINVAL: return "invalid argument (null pointer, negative size, K not a multiple of 128, N not a multiple of 8 (256 for the fused epilogue), K < 128, misaligned pointer, G < 1, unknown layout or scale kind)";
+    case FG_EINVAL: return "invalid argument (null pointer, negative size, K not a multiple of 128, N not a multiple of 8 (256 for the fused epilogue), K < 128, misaligned pointer, G < 1, unknown layout or scale kind, an operand of 2^31 bytes or more, N > 4194296)";
     case FG_EUNSUPPORTED: return "unsupported device (gfx950 required)";
     case FG_ELAUNCH: return "kernel launch failed";
     case FG_EDEVICE: return "HIP device query failed";

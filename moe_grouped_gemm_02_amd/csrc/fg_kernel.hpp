@@ -464,13 +464,46 @@ __device__ __forceinline__ void swiglu_quant_epilogue(const Params& p, const f32
 // One BM x BN output tile of expert g (dense: g = 0) whose first row is m0
 // and first column n0; rows_valid bounds the rows that have an output. The
 // tile sums K-blocks [kb0, kb0 + nkb) (nkb = 0: all of them, K / 128).
-template <int LAYOUT, class T, bool POW2, int EPI>
-__device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, int g, const int m0,
-                                          const int n0, const int rows_valid, const int kb0 = 0,
-                                          int nkb = 0) {
+// Column order of the B tile for the direct-store epilogue. The matrix core
+// gives lane (lr, lq) of a 16x16 sub-tile four consecutive columns 4lq..4lq+3;
+// loading the 32 weight rows of two neighbouring sub-tiles in the order
+// below makes that lane's columns of the pair 8lq..8lq+7 instead, one 16-byte
+// piece of an output row. LDS row R of a 32-row group (sub-tile R / 16, its
+// row R % 16) holds group column 8 * ((R % 16) / 4) + 4 * (R / 16) + R % 4.
+__device__ __forceinline__ int pair_column(int row) {
+  const int r = row & 31;
+  return (row & ~31) | (((r & 15) >> 2) << 3) | ((r >> 4) << 2) | (r & 3);
+}
+template <class T, int EPI>
+struct DirectStore {
+  // bf16 output written from the accumulators as 16-byte row pieces, without
+  // staging through LDS (needs whole sub-tile pairs within 32-column groups)
+  static constexpr bool value = EPI == kEpiBf16 && T::TN % 2 == 0 && T::WN % 32 == 0;
+};
+
+// One output tile: expert g (dense: 0), first row m0, first column n0, and
+// the bound on rows that have an output.
+struct TileDesc {
+  int g, m0, n0, rows_valid;
+};
+
+// The tiles a workgroup computes one after another: next(d) fills the next
+// tile and returns true, or returns false when the workgroup has no more
+// (uniform over the workgroup). Every tile sums K-blocks [kb0, kb0 + nkb)
+// (nkb = 0: all of them, K / 128).
+//
+// With the direct-store epilogue (DirectStore) the LDS ring is free once a
+// tile's K loop has ended, so the next tile's first stages are issued before
+// this tile's output stores: the loads' latency overlaps the stores, and the
+// stores drain while the next tile starts. Otherwise the epilogue stages the
+// output through LDS and the next tile starts after it.
+template <int LAYOUT, class T, bool POW2, int EPI, class Next>
+__device__ __forceinline__ void gemm_tiles(const Params& p, lds_u8* const lds, Next&& next, const int kb0 = 0,
+                                           int nkb = 0) {
   constexpr int BM = T::BM, BN = T::BN, W = T::W, WM = T::WM, WN = T::WN;
   constexpr int TM = T::TM, TN = T::TN, PD = T::PD, R = T::RING;
   constexpr int PL = T::PL, P = T::PARTS;
+  constexpr bool DIRECT = DirectStore<T, EPI>::value;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = uniform(t >> 6);
@@ -480,74 +513,110 @@ __device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, in
   const int wm = EPI == kEpiSwigluQuant ? wave % T::WGM : wave / T::WGN;
   const int wn = EPI == kEpiSwigluQuant ? wave / T::WGM : wave % T::WGN;
   const int lr = lane & 15, lq = lane >> 4;
-  g = uniform(g);
 
   const int K = p.K, KB = p.KB, M = p.M;
   if (nkb == 0) nkb = KB;
-  const uint8_t* Ag = p.A + (LAYOUT == kMasked ? (size_t)g * M * K : 0);
-  const float* sag = p.sa + (LAYOUT == kMasked ? (size_t)g * KB * M : 0);
-  const uint8_t* Bg = p.B + (LAYOUT != kDense ? (size_t)g * p.N * K : 0);
   const int NB128 = (p.N + 127) / 128;   // weight-scale row blocks (the last may be partial)
-  const float* sbg = p.sb + (LAYOUT != kDense ? (size_t)g * NB128 * KB : 0);
-  uint16_t* Dg = p.D + (LAYOUT == kMasked ? (size_t)g * M * p.N : 0);
-
-  const i32x4 rsA = buffer_rsrc(Ag, (uint32_t)M * (uint32_t)K);
-  const i32x4 rsB = buffer_rsrc(Bg, (uint32_t)p.N * (uint32_t)K);
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t wave_at = lds_addr + wave * 1024;   // this wave's 1 KB DMA slot in a tile region
 
-  // ---- DMA sources: a buffer resource per operand and per-lane byte offsets
-  // within one K-block column. Slot s of a tile region is the 16-byte LDS
-  // chunk s; it holds row s/8, chunk position s%8, i.e. global chunk
-  // (s%8) ^ (row%8). Rows that have no output -- padding slots past the tile,
-  // A rows past M, masked rows at or beyond masked_m[g], contiguous rows of
-  // padding or of another expert, B rows past N -- get the offset kNoRow,
+  // tile descriptors and the loop's branches are uniform over the workgroup
+  // (made explicit: a descriptor read from LDS would otherwise count as
+  // per-lane, and so would every buffer resource derived from it)
+  auto next_tile = [&](TileDesc& d) {
+    const bool more = uniform(next(d) ? 1 : 0) != 0;
+    d = TileDesc{uniform(d.g), uniform(d.m0), uniform(d.n0), uniform(d.rows_valid)};
+    return more;
+  };
+  TileDesc cur;
+  if (!next_tile(cur)) return;
+
+  // ---- per-tile DMA sources: a buffer resource per operand and per-lane
+  // byte offsets within one K-block column. Slot s of a tile region is the
+  // 16-byte LDS chunk s; it holds row s/8, chunk position s%8, i.e. global
+  // chunk (s%8) ^ (row%8). Rows that have no output -- padding slots past the
+  // tile, A rows past M, masked rows at or beyond masked_m[g], contiguous rows
+  // of padding or of another expert, B rows past N -- get the offset kNoRow,
   // beyond the operand's buffer: the range check returns zeros for them
   // without a memory access, so they cost no traffic and their MFMAs multiply
   // zeros (the matrix core draws less power on them).
-  uint32_t a_off[T::A_INSTR], b_off[T::B_INSTR];
-#pragma unroll
-  for (int q = 0; q < T::A_INSTR; ++q) {
-    const int slot = (q * W + wave) * 64 + lane;
-    const int row = slot >> 3, chunk = (slot & 7) ^ (row & 7);
-    const int m = m0 + row;
-    bool live = row < BM && m < rows_valid;
-    if (LAYOUT == kContiguous && live) live = p.m_indices[m] == g;
-    a_off[q] = live ? (uint32_t)m * (uint32_t)K + chunk * 16 : kNoRow;
-  }
-#pragma unroll
-  for (int q = 0; q < T::B_INSTR; ++q) {
-    const int slot = (q * W + wave) * 64 + lane;
-    const int row = slot >> 3, chunk = (slot & 7) ^ (row & 7);
-    const int n = n0 + row;
-    b_off[q] = row < BN && n < p.N ? (uint32_t)n * (uint32_t)K + chunk * 16 : kNoRow;
-  }
+  i32x4 rsA, rsB, rsS[T::SC_INSTR];
+  uint32_t a_off[T::A_INSTR], b_off[T::B_INSTR], sc_off[T::SC_INSTR];
+  int nb_lo, nb_hi, j_switch;
   // Scale loads: load i = q*W + wave brings activation rows [64i, 64i+64)
   // (i < BM/64) or the weight scales of the tile's 128-column blocks
   // (i == BM/64, clamped); a wave without a load of its own repeats load 0.
-  const int nb_tile = n0 >> 7;
-  const i32x4 rsSA = buffer_rsrc(sag, (uint32_t)KB * (uint32_t)M * 4u);
-  const i32x4 rsSB = buffer_rsrc(sbg, (uint32_t)NB128 * (uint32_t)KB * 4u);
-  i32x4 rsS[T::SC_INSTR];
-  uint32_t sc_off[T::SC_INSTR], sc_stride[T::SC_INSTR], sc_dst[T::SC_INSTR];
+  int sc_row[T::SC_INSTR];   // i * 64, or -1 for the weight-scale load
+  uint32_t sc_stride[T::SC_INSTR], sc_dst[T::SC_INSTR];
 #pragma unroll
   for (int q = 0; q < T::SC_INSTR; ++q) {
     int i = q * W + wave;
     if (i >= T::SC_LOADS) i = 0;
     const bool is_b = i == BM / 64;
-    rsS[q] = is_b ? rsSB : rsSA;
+    sc_row[q] = is_b ? -1 : i * 64;
     sc_stride[q] = is_b ? 4u : (uint32_t)M * 4u;
     sc_dst[q] = lds_addr + T::SC_BASE + (is_b ? BM * 4 : i * 256);
-    // weight scales: a tile reads at most the blocks nb_tile .. nb_tile+2, so
-    // lanes past 3 repeat lane 3's row (one cache line instead of one per lane)
-    sc_off[q] = is_b ? (uint32_t)min(nb_tile + min(lane, 3), NB128 - 1) * (uint32_t)KB * 4u
-                     : (uint32_t)min(m0 + i * 64 + lane, M - 1) * 4u;
   }
-  const uint32_t wave_at = lds_addr + wave * 1024;   // this wave's 1 KB DMA slot in a tile region
+  // ---- per-lane LDS addresses of this wave's fragments and scales. Chunk c
+  // of tile row r sits at r*128 + ((c ^ (r & 7)) << 4); a wave's fragments
+  // start at multiples of 16 rows, so r & 7 == lr & 7 and every fragment is
+  // one of four per-lane bases plus a compile-time offset.
+  constexpr int NWIN = (T::RING_BYTES + 65535) >> 16;
+  LdsAddr<NWIN> aLo, aHi, bLo, bHi, sA, sB0, sB1;
+  {
+    const uint32_t lane_lo = lr * 128 + ((lq ^ (lr & 7)) << 4);
+    const uint32_t lane_hi = lr * 128 + (((lq + 4) ^ (lr & 7)) << 4);
+    aLo.init(lds_addr + wm * WM * 128 + lane_lo);
+    aHi.init(lds_addr + wm * WM * 128 + lane_hi);
+    bLo.init(lds_addr + wn * WN * 128 + lane_lo);
+    bHi.init(lds_addr + wn * WN * 128 + lane_hi);
+    sA.init(lds_addr + (wm * WM + lr) * 4);
+  }
+  auto setup = [&](const TileDesc& d) {
+    const int g = d.g, m0 = d.m0, n0 = d.n0, rows_valid = d.rows_valid;
+    const uint8_t* Ag = p.A + (LAYOUT == kMasked ? (size_t)g * M * K : 0);
+    const float* sag = p.sa + (LAYOUT == kMasked ? (size_t)g * KB * M : 0);
+    const uint8_t* Bg = p.B + (LAYOUT != kDense ? (size_t)g * p.N * K : 0);
+    const float* sbg = p.sb + (LAYOUT != kDense ? (size_t)g * NB128 * KB : 0);
+    rsA = buffer_rsrc(Ag, (uint32_t)M * (uint32_t)K);
+    rsB = buffer_rsrc(Bg, (uint32_t)p.N * (uint32_t)K);
+#pragma unroll
+    for (int q = 0; q < T::A_INSTR; ++q) {
+      const int slot = (q * W + wave) * 64 + lane;
+      const int row = slot >> 3, chunk = (slot & 7) ^ (row & 7);
+      const int m = m0 + row;
+      bool live = row < BM && m < rows_valid;
+      if (LAYOUT == kContiguous && live) live = p.m_indices[m] == g;
+      a_off[q] = live ? (uint32_t)m * (uint32_t)K + chunk * 16 : kNoRow;
+    }
+#pragma unroll
+    for (int q = 0; q < T::B_INSTR; ++q) {
+      const int slot = (q * W + wave) * 64 + lane;
+      const int row = slot >> 3, chunk = (slot & 7) ^ (row & 7);
+      const int n = n0 + (DIRECT ? pair_column(row) : row);
+      b_off[q] = row < BN && n < p.N ? (uint32_t)n * (uint32_t)K + chunk * 16 : kNoRow;
+    }
+    const int nb_tile = n0 >> 7;
+    const i32x4 rsSA = buffer_rsrc(sag, (uint32_t)KB * (uint32_t)M * 4u);
+    const i32x4 rsSB = buffer_rsrc(sbg, (uint32_t)NB128 * (uint32_t)KB * 4u);
+#pragma unroll
+    for (int q = 0; q < T::SC_INSTR; ++q) {
+      const bool is_b = sc_row[q] < 0;
+      rsS[q] = is_b ? rsSB : rsSA;
+      // weight scales: a tile reads at most the blocks nb_tile .. nb_tile+2, so
+      // lanes past 3 repeat lane 3's row (one cache line instead of one per lane)
+      sc_off[q] = is_b ? (uint32_t)min(nb_tile + min(lane, 3), NB128 - 1) * (uint32_t)KB * 4u
+                       : (uint32_t)min(m0 + sc_row[q] + lane, M - 1) * 4u;
+    }
+    // scale blocks of B covered by this wave's columns (at most two) and the
+    // first sub-tile column whose scale block is nb_hi
+    const int wn0 = n0 + wn * WN;
+    nb_lo = uniform(min(wn0 >> 7, NB128 - 1));
+    nb_hi = uniform(min(nb_lo + 1, NB128 - 1));
+    j_switch = T::STRADDLE ? uniform(((nb_lo + 1) * 128 - wn0) >> 4) : TN;
+    sB0.init(lds_addr + (BM + nb_lo - nb_tile) * 4);
+    sB1.init(lds_addr + (BM + nb_hi - nb_tile) * 4);
+  };
 
   // Scalar offsets of one DMA group: the A tile and scales of K-block ka and
   // the B tile of K-block kbb (the two rings run different distances ahead).
@@ -578,30 +647,6 @@ __device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, in
     }
   };
 
-  // ---- scale blocks of B covered by this wave's columns (at most two)
-  const int wn0 = n0 + wn * WN;
-  const int nb_lo = uniform(min(wn0 >> 7, NB128 - 1));
-  const int nb_hi = uniform(min(nb_lo + 1, NB128 - 1));
-  // first sub-tile column whose scale block is nb_hi
-  const int j_switch = T::STRADDLE ? uniform(((nb_lo + 1) * 128 - wn0) >> 4) : TN;
-
-  // ---- per-lane LDS addresses of this wave's fragments and scales. Chunk c
-  // of tile row r sits at r*128 + ((c ^ (r & 7)) << 4); a wave's fragments
-  // start at multiples of 16 rows, so r & 7 == lr & 7 and every fragment is
-  // one of four per-lane bases plus a compile-time offset.
-  constexpr int NWIN = (T::RING_BYTES + 65535) >> 16;
-  LdsAddr<NWIN> aLo, aHi, bLo, bHi, sA, sB0, sB1;
-  {
-    const uint32_t lane_lo = lr * 128 + ((lq ^ (lr & 7)) << 4);
-    const uint32_t lane_hi = lr * 128 + (((lq + 4) ^ (lr & 7)) << 4);
-    aLo.init(lds_addr + wm * WM * 128 + lane_lo);
-    aHi.init(lds_addr + wm * WM * 128 + lane_hi);
-    bLo.init(lds_addr + wn * WN * 128 + lane_lo);
-    bHi.init(lds_addr + wn * WN * 128 + lane_hi);
-    sA.init(lds_addr + (wm * WM + lr) * 4);
-    sB0.init(lds_addr + (BM + nb_lo - nb_tile) * 4);
-    sB1.init(lds_addr + (BM + nb_hi - nb_tile) * 4);
-  }
   // A fragment i / B fragment j of ring stage ST
   auto fragA = [&](auto st_c, auto i_c) {
     return frag_at<T::A_BASE + decltype(st_c)::value * T::A_BYTES + decltype(i_c)::value * 2048>(aLo, aHi);
@@ -646,255 +691,347 @@ __device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, in
 
   // ---- prologue: the groups g(-SB) .. g(-1) (the last one only its head),
   // i.e. the B tiles of K-blocks 0 .. SB-1 and the A tiles of 0 .. SA-1, then
-  // wait for K-block 0
-  if constexpr (SPLIT) {
-    static_for<2>([&](auto x_c) {
-      constexpr int x = decltype(x_c)::value;
-      const Soff o = soff_of(min(x, nkb - 1), min(x, nkb - 1));
-      static_for<D>([&](auto d_c) { issue(d_c, x_c, x_c, o); });
-    });
-  } else {
-    static_for<SB>([&](auto x_c) {
-      constexpr int x = decltype(x_c)::value;       // group g(x - SB)
-      constexpr int ka = x - SB + SA;               // its A K-block (< 0: none)
-      const Soff o = soff_of(min(ka < 0 ? 0 : ka, nkb - 1), min(x, nkb - 1));
-      static_for<D>([&](auto d_c) {
-        constexpr int d = decltype(d_c)::value;
-        constexpr bool a_part = d < NA + NSC;
-        if constexpr (!(a_part && ka < 0) && !(x == SB - 1 && SCH::slot(d) >= POST))
-          issue(d_c, std::integral_constant<int, (ka < 0 ? 0 : ka)>{}, x_c, o);
+  // wait for K-block 0 (after the previous tile's output stores, if they were
+  // issued after this prologue)
+  auto prologue = [&]() {
+    if constexpr (SPLIT) {
+      static_for<2>([&](auto x_c) {
+        constexpr int x = decltype(x_c)::value;
+        const Soff o = soff_of(min(x, nkb - 1), min(x, nkb - 1));
+        static_for<D>([&](auto d_c) { issue(d_c, x_c, x_c, o); });
       });
-    });
-  }
-  wait_vm<WAIT_PRO>();
-  block_barrier();
-
-  // Register state. B fragments live in a ring of R = PD+1 (column g of the
-  // K-block sequence, counting columns across K-blocks, in slot g % R); column
-  // j+PD is read while column j computes. A fragments are held for the whole
-  // K-block; with FA2 the K-blocks alternate between two sets and the next
-  // K-block's set is read right after the barrier. Scales alternate between
-  // two sets as well: a K-block's own and its predecessor's, which the first
-  // PL steps still need for the carried promotions.
-  i32x8 fbr[R], fa[T::FA2 ? 2 : 1][TM];
-  float sc_lo[2][TM], sc_hi[2][TM];
-  int ea[2][TM], eb_lo[2], eb_hi[2];   // POW2: E8M0 codes of the two scale sets
-  f32x4 part[P];
-  auto scale_read = [&](auto st_c, float (&a)[TM], float& b0, float& b1) {
-    constexpr int ST = decltype(st_c)::value;
-    static_for<TM>([&](auto i_c) {
-      a[decltype(i_c)::value] = f32_at<T::SC_BASE + ST * T::SC_BYTES + decltype(i_c)::value * 64>(sA);
-    });
-    b0 = f32_at<T::SC_BASE + ST * T::SC_BYTES>(sB0);
-    b1 = f32_at<T::SC_BASE + ST * T::SC_BYTES>(sB1);
-  };
-  auto set_scales = [&](auto set_c, const float (&a)[TM], float b0, float b1) {
-    constexpr int SET = decltype(set_c)::value;
-    if constexpr (POW2) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) ea[SET][i] = e8m0_of(a[i]);
-      eb_lo[SET] = e8m0_of(b0);
-      eb_hi[SET] = T::STRADDLE ? e8m0_of(b1) : 0;
     } else {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        sc_lo[SET][i] = a[i] * b0;
-        sc_hi[SET][i] = T::STRADDLE ? a[i] * b1 : 0.f;
-      }
-    }
-  };
-  // scale of sub-tile (pi, pj) from scale set SET (a value select: selecting
-  // between the two array elements themselves would keep the arrays in memory)
-  auto scale_of = [&](auto set_c, auto pi_c, auto pj_c) {
-    constexpr int SET = decltype(set_c)::value, pi = decltype(pi_c)::value, pj = decltype(pj_c)::value;
-    const float lo = sc_lo[SET][pi];
-    if constexpr (!T::STRADDLE) return lo;
-    const float hi = sc_hi[SET][pi];
-    return pj >= j_switch ? hi : lo;
-  };
-
-  // Stage 0's reads are issued in the order in which the loop itself leaves
-  // the next stage's reads in flight (scales, then FA2 ? A, B : B, A). The
-  // compiler places one LDS wait at the loop head that must hold for both the
-  // entry and the back edge; with matching orders it is the steady-state wait
-  // instead of a full drain on every K-block.
-  {
-    using Z = std::integral_constant<int, 0>;
-    float a0[TM], b0, b1;
-    scale_read(Z{}, a0, b0, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (T::FA2) {
-      static_for<TM>([&](auto i_c) {
-        fa[0][decltype(i_c)::value] = fragA(Z{}, i_c);
-        __builtin_amdgcn_sched_barrier(0);
+      static_for<SB>([&](auto x_c) {
+        constexpr int x = decltype(x_c)::value;       // group g(x - SB)
+        constexpr int ka = x - SB + SA;               // its A K-block (< 0: none)
+        const Soff o = soff_of(min(ka < 0 ? 0 : ka, nkb - 1), min(x, nkb - 1));
+        static_for<D>([&](auto d_c) {
+          constexpr int d = decltype(d_c)::value;
+          constexpr bool a_part = d < NA + NSC;
+          if constexpr (!(a_part && ka < 0) && !(x == SB - 1 && SCH::slot(d) >= POST))
+            issue(d_c, std::integral_constant<int, (ka < 0 ? 0 : ka)>{}, x_c, o);
+        });
       });
     }
-    static_for<PD>([&](auto c_c) {
-      fbr[decltype(c_c)::value] = fragB(Z{}, c_c);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    if constexpr (!T::FA2) {
-      static_for<TM>([&](auto i_c) {
-        fa[0][decltype(i_c)::value] = fragA(Z{}, i_c);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    }
-    set_scales(std::integral_constant<int, 0>{}, a0, b0, b1);
-  }
-  // before K-block 0 nothing is pending: zero partials promoted with zero
-  // scales leave the (zero) accumulators unchanged
-  if constexpr (!POW2) {
-#pragma unroll
-    for (int c = 0; c < P; ++c) part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < TM; ++i) sc_lo[1][i] = sc_hi[1][i] = 0.f;
-  }
-
-  // promotion of MFMA u - PL of a K-block with phase PH (for u < PL: MFMA
-  // STEPS + u - PL of the previous K-block, with the previous scale set)
-  auto promote_step = [&](auto ph_c, auto u_c) {
-    constexpr int PH = decltype(ph_c)::value, u = decltype(u_c)::value;
-    constexpr int v = u - PL;
-    constexpr int w = v >= 0 ? v : v + STEPS;
-    constexpr int pj = w / TM, pi = w % TM;
-    constexpr int set = v >= 0 ? (PH & 1) : ((PH + 1) & 1);
-    promote(acc[pi][pj], part[(PH * STEPS + v + T::UNROLL * STEPS) % P],
-            scale_of(std::integral_constant<int, set>{}, std::integral_constant<int, pi>{},
-                     std::integral_constant<int, pj>{}));
   };
-
-  // One K-block with compile-time phase PH = kb % U: TM x TN MFMAs in column
-  // order. Step u issues MFMA u and then promotes MFMA u-PL. An MFMA's result
-  // arrives well after the next MFMA could issue; waiting PL MFMAs before
-  // reading it keeps the VALU work off the matrix core's critical path even
-  // with a single wave per SIMD. The barrier sits before column JB = TN-PD,
-  // when every read of the current stage has been issued; after it the next
-  // stage's scales, first PD B fragments and (FA2) A fragments are read, or
-  // (otherwise) each fa[i] is replaced right after its last MFMA.
-  int kb = 0;
-  auto kblock = [&](auto ph_c) -> bool {
-    constexpr int PH = decltype(ph_c)::value;
-    constexpr int U = T::UNROLL;
-    constexpr int CA = PH % SA, NXA = (PH + 1) % SA, TA = (PH + U - 1) % SA;   // A ring: this, next, tail group
-    constexpr int CB = PH % SB, NXB = (PH + 1) % SB, TB = (PH + U - 1) % SB;   // B ring
-    constexpr int FSET = T::FA2 ? (PH & 1) : 0, NFSET = T::FA2 ? ((PH + 1) & 1) : 0;
-    using CurA = std::integral_constant<int, CA>;
-    using NxtA = std::integral_constant<int, NXA>;
-    using CurB = std::integral_constant<int, CB>;
-    using NxtB = std::integral_constant<int, NXB>;
-    const Soff head = soff_of(min(kb + SA, nkb - 1), min(kb + SB, nkb - 1));           // group g(kb)
-    const Soff tail = soff_of(min(kb - 1 + SA, nkb - 1), min(kb - 1 + SB, nkb - 1));   // group g(kb-1)
-    (void)tail;
-    float sa_next[TM], sb_next0 = 0.f, sb_next1 = 0.f;
-    static_for<STEPS>([&](auto u_c) {
-      constexpr int u = decltype(u_c)::value;
-      constexpr int j = u / TM, i = u % TM;
-      if constexpr (SPLIT && u == TM && TM < PRE) block_barrier();   // A half of this stage is free
-      if constexpr (u == PRE) {
-        // every read of the current stage has been issued; the next stage (and,
-        // for S == 2, every DMA older than this K-block's early A loads) is in
-        wait_lgkm0();
-        wait_vm<WAIT_LOOP>();
-        block_barrier();
-        scale_read(NxtA{}, sa_next, sb_next0, sb_next1);
-        if constexpr (T::FA2) {
-          static_for<TM>([&](auto ii_c) { fa[NFSET][decltype(ii_c)::value] = fragA(NxtA{}, ii_c); });
-        }
-      }
-      if constexpr (POW2) {
-        // this K-block's scales are set PH & 1 (K-blocks alternate sets)
-        constexpr int SET = PH & 1;
-        int eb = eb_lo[SET];
-        if constexpr (T::STRADDLE) eb = j >= j_switch ? eb_hi[SET] : eb_lo[SET];
-        acc[i][j] = mfma_e4m3_pow2(fbr[(PH * TN + j) % R], fa[FSET][i], acc[i][j], eb, ea[SET][i]);
-      } else {
-        part[(PH * STEPS + u) % P] = mfma_e4m3(fbr[(PH * TN + j) % R], fa[FSET][i]);
-      }
-      if constexpr (i == 0) {
-        // column j+PD of this stage, or (past the end) column j+PD-TN of the next
-        constexpr int jn = j + PD;
-        constexpr int slot = (PH * TN + jn) % R;
-        if constexpr (jn < TN) fbr[slot] = fragB(CurB{}, std::integral_constant<int, jn>{});
-        else fbr[slot] = fragB(NxtB{}, std::integral_constant<int, jn - TN>{});
-      }
-      if constexpr (!T::FA2 && j == TN - 1) fa[0][i] = fragA(NxtA{}, std::integral_constant<int, i>{});
-      static_for<D>([&](auto d_c) {
-        constexpr int d = decltype(d_c)::value;
-        if constexpr (SPLIT) {
-          if constexpr (SCH::slot(d) == u) issue(d_c, CurA{}, CurB{}, head);   // K-block kb+2
-        } else {
-          if constexpr (u >= PRE && SCH::slot(d) == u - PRE) issue(d_c, CurA{}, CurB{}, head);
-          if constexpr (u < PRE && SCH::slot(d) == POST + u)
-            issue(d_c, std::integral_constant<int, TA>{}, std::integral_constant<int, TB>{}, tail);
-        }
-      });
-      if constexpr (!POW2) promote_step(ph_c, u_c);
-      step_fence();
-    });
-    set_scales(std::integral_constant<int, (PH + 1) & 1>{}, sa_next, sb_next0, sb_next1);
-    return ++kb == nkb;
-  };
-  bool done = false;
+  constexpr int NST = DIRECT ? TM * (TN / 2) : 0;   // output stores per wave and tile (direct epilogue)
+  static_assert(WAIT_PRO + NST < 64, "vmcnt counter range");
+  setup(cur);
+  prologue();
+  bool after_stores = false;   // the previous tile's NST stores were issued after this tile's prologue
   for (;;) {
-    static_for<T::UNROLL>([&](auto ph_c) {
-      if (!done) done = kblock(ph_c);
-    });
-    if (done) break;
-  }
-  // The last K-block's final PL partials, promoted once after the loop (an
-  // exit path per phase that did this work would keep the register allocator
-  // from holding each accumulator in one register across the phases).
-  if constexpr (!POW2) {
-    const int last = (nkb - 1) % T::UNROLL;
-    static_for<T::UNROLL>([&](auto ph_c) {
-      constexpr int PH = decltype(ph_c)::value;
-      if (last == PH) {
-        static_for<PL>([&](auto c_c) {
-          constexpr int w = STEPS - PL + decltype(c_c)::value;
-          promote(acc[w % TM][w / TM], part[(PH * STEPS + w) % P],
-                  scale_of(std::integral_constant<int, PH & 1>{}, std::integral_constant<int, w % TM>{},
-                           std::integral_constant<int, w / TM>{}));
+    if (after_stores) {
+      wait_vm<WAIT_PRO + NST>();
+    } else {
+      wait_vm<WAIT_PRO>();
+    }
+    block_barrier();
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Register state. B fragments live in a ring of R = PD+1 (column g of the
+    // K-block sequence, counting columns across K-blocks, in slot g % R); column
+    // j+PD is read while column j computes. A fragments are held for the whole
+    // K-block; with FA2 the K-blocks alternate between two sets and the next
+    // K-block's set is read right after the barrier. Scales alternate between
+    // two sets as well: a K-block's own and its predecessor's, which the first
+    // PL steps still need for the carried promotions.
+    i32x8 fbr[R], fa[T::FA2 ? 2 : 1][TM];
+    float sc_lo[2][TM], sc_hi[2][TM];
+    int ea[2][TM], eb_lo[2], eb_hi[2];   // POW2: E8M0 codes of the two scale sets
+    f32x4 part[P];
+    auto scale_read = [&](auto st_c, float (&a)[TM], float& b0, float& b1) {
+      constexpr int ST = decltype(st_c)::value;
+      static_for<TM>([&](auto i_c) {
+        a[decltype(i_c)::value] = f32_at<T::SC_BASE + ST * T::SC_BYTES + decltype(i_c)::value * 64>(sA);
+      });
+      b0 = f32_at<T::SC_BASE + ST * T::SC_BYTES>(sB0);
+      b1 = f32_at<T::SC_BASE + ST * T::SC_BYTES>(sB1);
+    };
+    auto set_scales = [&](auto set_c, const float (&a)[TM], float b0, float b1) {
+      constexpr int SET = decltype(set_c)::value;
+      if constexpr (POW2) {
+  #pragma unroll
+        for (int i = 0; i < TM; ++i) ea[SET][i] = e8m0_of(a[i]);
+        eb_lo[SET] = e8m0_of(b0);
+        eb_hi[SET] = T::STRADDLE ? e8m0_of(b1) : 0;
+      } else {
+  #pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          sc_lo[SET][i] = a[i] * b0;
+          sc_hi[SET][i] = T::STRADDLE ? a[i] * b1 : 0.f;
+        }
+      }
+    };
+    // scale of sub-tile (pi, pj) from scale set SET (a value select: selecting
+    // between the two array elements themselves would keep the arrays in memory)
+    auto scale_of = [&](auto set_c, auto pi_c, auto pj_c) {
+      constexpr int SET = decltype(set_c)::value, pi = decltype(pi_c)::value, pj = decltype(pj_c)::value;
+      const float lo = sc_lo[SET][pi];
+      if constexpr (!T::STRADDLE) return lo;
+      const float hi = sc_hi[SET][pi];
+      return pj >= j_switch ? hi : lo;
+    };
+
+    // Stage 0's reads are issued in the order in which the loop itself leaves
+    // the next stage's reads in flight (scales, then FA2 ? A, B : B, A). The
+    // compiler places one LDS wait at the loop head that must hold for both the
+    // entry and the back edge; with matching orders it is the steady-state wait
+    // instead of a full drain on every K-block.
+    {
+      using Z = std::integral_constant<int, 0>;
+      float a0[TM], b0, b1;
+      scale_read(Z{}, a0, b0, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (T::FA2) {
+        static_for<TM>([&](auto i_c) {
+          fa[0][decltype(i_c)::value] = fragA(Z{}, i_c);
+          __builtin_amdgcn_sched_barrier(0);
         });
       }
-    });
-  }
+      static_for<PD>([&](auto c_c) {
+        fbr[decltype(c_c)::value] = fragB(Z{}, c_c);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if constexpr (!T::FA2) {
+        static_for<TM>([&](auto i_c) {
+          fa[0][decltype(i_c)::value] = fragA(Z{}, i_c);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      set_scales(std::integral_constant<int, 0>{}, a0, b0, b1);
+    }
+    // before K-block 0 nothing is pending: zero partials promoted with zero
+    // scales leave the (zero) accumulators unchanged
+    if constexpr (!POW2) {
+  #pragma unroll
+      for (int c = 0; c < P; ++c) part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int i = 0; i < TM; ++i) sc_lo[1][i] = sc_hi[1][i] = 0.f;
+    }
 
+    // promotion of MFMA u - PL of a K-block with phase PH (for u < PL: MFMA
+    // STEPS + u - PL of the previous K-block, with the previous scale set)
+    auto promote_step = [&](auto ph_c, auto u_c) {
+      constexpr int PH = decltype(ph_c)::value, u = decltype(u_c)::value;
+      constexpr int v = u - PL;
+      constexpr int w = v >= 0 ? v : v + STEPS;
+      constexpr int pj = w / TM, pi = w % TM;
+      constexpr int set = v >= 0 ? (PH & 1) : ((PH + 1) & 1);
+      promote(acc[pi][pj], part[(PH * STEPS + v + T::UNROLL * STEPS) % P],
+              scale_of(std::integral_constant<int, set>{}, std::integral_constant<int, pi>{},
+                       std::integral_constant<int, pj>{}));
+    };
 
-  wait_vm<0>();          // the clamped tail DMAs must land before LDS is reused
-  wait_lgkm0();
-  block_barrier();
-  if constexpr (EPI == kEpiSwigluQuant) {
-    swiglu_quant_epilogue<LAYOUT, T, POW2>(p, acc, lds, g, m0, n0, rows_valid, wm, wn, lr, lq, t);
-    return;
-  }
-  // ---- epilogue: bf16 RNE, staged through LDS so that every global store is
-  // a full 16-byte piece of a contiguous output row
-  constexpr int ROWB = T::ROWB;
+    // One K-block with compile-time phase PH = kb % U: TM x TN MFMAs in column
+    // order. Step u issues MFMA u and then promotes MFMA u-PL. An MFMA's result
+    // arrives well after the next MFMA could issue; waiting PL MFMAs before
+    // reading it keeps the VALU work off the matrix core's critical path even
+    // with a single wave per SIMD. The barrier sits before column JB = TN-PD,
+    // when every read of the current stage has been issued; after it the next
+    // stage's scales, first PD B fragments and (FA2) A fragments are read, or
+    // (otherwise) each fa[i] is replaced right after its last MFMA.
+    int kb = 0;
+    auto kblock = [&](auto ph_c) -> bool {
+      constexpr int PH = decltype(ph_c)::value;
+      constexpr int U = T::UNROLL;
+      constexpr int CA = PH % SA, NXA = (PH + 1) % SA, TA = (PH + U - 1) % SA;   // A ring: this, next, tail group
+      constexpr int CB = PH % SB, NXB = (PH + 1) % SB, TB = (PH + U - 1) % SB;   // B ring
+      constexpr int FSET = T::FA2 ? (PH & 1) : 0, NFSET = T::FA2 ? ((PH + 1) & 1) : 0;
+      using CurA = std::integral_constant<int, CA>;
+      using NxtA = std::integral_constant<int, NXA>;
+      using CurB = std::integral_constant<int, CB>;
+      using NxtB = std::integral_constant<int, NXB>;
+      const Soff head = soff_of(min(kb + SA, nkb - 1), min(kb + SB, nkb - 1));           // group g(kb)
+      const Soff tail = soff_of(min(kb - 1 + SA, nkb - 1), min(kb - 1 + SB, nkb - 1));   // group g(kb-1)
+      (void)tail;
+      float sa_next[TM], sb_next0 = 0.f, sb_next1 = 0.f;
+      static_for<STEPS>([&](auto u_c) {
+        constexpr int u = decltype(u_c)::value;
+        constexpr int j = u / TM, i = u % TM;
+        if constexpr (SPLIT && u == TM && TM < PRE) block_barrier();   // A half of this stage is free
+        if constexpr (u == PRE) {
+          // every read of the current stage has been issued; the next stage (and,
+          // for S == 2, every DMA older than this K-block's early A loads) is in
+          wait_lgkm0();
+          wait_vm<WAIT_LOOP>();
+          block_barrier();
+          scale_read(NxtA{}, sa_next, sb_next0, sb_next1);
+          if constexpr (T::FA2) {
+            static_for<TM>([&](auto ii_c) { fa[NFSET][decltype(ii_c)::value] = fragA(NxtA{}, ii_c); });
+          }
+        }
+        if constexpr (POW2) {
+          // this K-block's scales are set PH & 1 (K-blocks alternate sets)
+          constexpr int SET = PH & 1;
+          int eb = eb_lo[SET];
+          if constexpr (T::STRADDLE) eb = j >= j_switch ? eb_hi[SET] : eb_lo[SET];
+          acc[i][j] = mfma_e4m3_pow2(fbr[(PH * TN + j) % R], fa[FSET][i], acc[i][j], eb, ea[SET][i]);
+        } else {
+          part[(PH * STEPS + u) % P] = mfma_e4m3(fbr[(PH * TN + j) % R], fa[FSET][i]);
+        }
+        if constexpr (i == 0) {
+          // column j+PD of this stage, or (past the end) column j+PD-TN of the next
+          constexpr int jn = j + PD;
+          constexpr int slot = (PH * TN + jn) % R;
+          if constexpr (jn < TN) fbr[slot] = fragB(CurB{}, std::integral_constant<int, jn>{});
+          else fbr[slot] = fragB(NxtB{}, std::integral_constant<int, jn - TN>{});
+        }
+        if constexpr (!T::FA2 && j == TN - 1) fa[0][i] = fragA(NxtA{}, std::integral_constant<int, i>{});
+        static_for<D>([&](auto d_c) {
+          constexpr int d = decltype(d_c)::value;
+          if constexpr (SPLIT) {
+            if constexpr (SCH::slot(d) == u) issue(d_c, CurA{}, CurB{}, head);   // K-block kb+2
+          } else {
+            if constexpr (u >= PRE && SCH::slot(d) == u - PRE) issue(d_c, CurA{}, CurB{}, head);
+            if constexpr (u < PRE && SCH::slot(d) == POST + u)
+              issue(d_c, std::integral_constant<int, TA>{}, std::integral_constant<int, TB>{}, tail);
+          }
+        });
+        if constexpr (!POW2) promote_step(ph_c, u_c);
+        step_fence();
+      });
+      set_scales(std::integral_constant<int, (PH + 1) & 1>{}, sa_next, sb_next0, sb_next1);
+      return ++kb == nkb;
+    };
+    bool done = false;
+    for (;;) {
+      static_for<T::UNROLL>([&](auto ph_c) {
+        if (!done) done = kblock(ph_c);
+      });
+      if (done) break;
+    }
+    // The last K-block's final PL partials, promoted once after the loop (an
+    // exit path per phase that did this work would keep the register allocator
+    // from holding each accumulator in one register across the phases).
+    if constexpr (!POW2) {
+      const int last = (nkb - 1) % T::UNROLL;
+      static_for<T::UNROLL>([&](auto ph_c) {
+        constexpr int PH = decltype(ph_c)::value;
+        if (last == PH) {
+          static_for<PL>([&](auto c_c) {
+            constexpr int w = STEPS - PL + decltype(c_c)::value;
+            promote(acc[w % TM][w / TM], part[(PH * STEPS + w) % P],
+                    scale_of(std::integral_constant<int, PH & 1>{}, std::integral_constant<int, w % TM>{},
+                             std::integral_constant<int, w / TM>{}));
+          });
+        }
+      });
+    }
+
+    const int g = cur.g, m0 = cur.m0, n0 = cur.n0, rows_valid = cur.rows_valid;
+    uint16_t* Dg = p.D + (LAYOUT == kMasked ? (size_t)g * M * p.N : 0);
+    wait_vm<0>();          // the clamped tail DMAs must land before LDS is reused
+    wait_lgkm0();
+    block_barrier();
+    if constexpr (DIRECT) {
+      // bf16 RNE straight from the accumulators: sub-tiles 2q and 2q+1 hold
+      // columns 32q + 8lq .. 32q + 8lq + 7 of row 16i + lr (the B tile was
+      // loaded in pair_column order). Stores go through a buffer resource
+      // over this tile's output rows, so a row or column without an output
+      // gets an offset past it and its store is dropped: every wave issues
+      // exactly NST stores, which the next tile's first wait counts. N is a
+      // multiple of 8, so a 16-byte piece is wholly inside or wholly past N.
+      const int rows_here = max(0, min(rows_valid - m0, BM));
+      const __amdgpu_buffer_rsrc_t rsD =
+          __builtin_amdgcn_make_buffer_rsrc(Dg + (size_t)m0 * p.N, 0, rows_here * p.N * 2, 0x20000);
+      uint32_t roff[TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int ml = wm * WM + i * 16 + lr;
+      for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * WM + i * 16 + lr;
+        bool ok = m < rows_valid;
+        if (LAYOUT == kContiguous && ok) ok = p.m_indices[m] == g;
+        roff[i] = ok ? (uint32_t)(m - m0) * (uint32_t)p.N * 2u : kNoRow;
+        // any m_indices load completes here, before the next tile's DMAs are
+        // in flight (a later wait for it would also wait for them)
+        asm volatile("" : "+v"(roff[i]));
+      }
+      TileDesc nx;
+      const bool more = next_tile(nx);
+      if (more) {
+        setup(nx);
+        prologue();
+      }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int nl = wn * WN + j * 16 + 4 * lq;
-      const uint32_t lo = bf16_rne_bits(acc[i][j][0]) | (bf16_rne_bits(acc[i][j][1]) << 16);
-      const uint32_t hi = bf16_rne_bits(acc[i][j][2]) | (bf16_rne_bits(acc[i][j][3]) << 16);
-      *(__attribute__((address_space(3))) u32x2*)(lds + ml * ROWB + nl * 2) = u32x2{lo, hi};
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int q = 0; q < TN / 2; ++q) {
+          const int n = n0 + wn * WN + q * 32 + lq * 8;
+          const uint32_t off = n < p.N ? roff[i] + (uint32_t)n * 2u : kNoRow;
+          const f32x4& x = acc[i][2 * q];
+          const f32x4& y = acc[i][2 * q + 1];
+          const i32x4 v = {(int)(bf16_rne_bits(x[0]) | (bf16_rne_bits(x[1]) << 16)),
+                           (int)(bf16_rne_bits(x[2]) | (bf16_rne_bits(x[3]) << 16)),
+                           (int)(bf16_rne_bits(y[0]) | (bf16_rne_bits(y[1]) << 16)),
+                           (int)(bf16_rne_bits(y[2]) | (bf16_rne_bits(y[3]) << 16))};
+          __builtin_amdgcn_raw_buffer_store_b128(v, rsD, off, 0, 0);
+        }
+      if (!more) break;
+      cur = nx;
+      after_stores = true;
+    } else {
+      if constexpr (EPI == kEpiSwigluQuant) {
+        swiglu_quant_epilogue<LAYOUT, T, POW2>(p, acc, lds, g, m0, n0, rows_valid, wm, wn, lr, lq, t);
+      } else {
+        // ---- epilogue: bf16 RNE, staged through LDS so that every global store is
+        // a full 16-byte piece of a contiguous output row
+        constexpr int ROWB = T::ROWB;
+      #pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int ml = wm * WM + i * 16 + lr;
+      #pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int nl = wn * WN + j * 16 + 4 * lq;
+            const uint32_t lo = bf16_rne_bits(acc[i][j][0]) | (bf16_rne_bits(acc[i][j][1]) << 16);
+            const uint32_t hi = bf16_rne_bits(acc[i][j][2]) | (bf16_rne_bits(acc[i][j][3]) << 16);
+            *(__attribute__((address_space(3))) u32x2*)(lds + ml * ROWB + nl * 2) = u32x2{lo, hi};
+          }
+        }
+        wait_lgkm0();
+        block_barrier();
+        constexpr int CPR = BN * 2 / 16;   // 16-byte pieces per output row
+      #pragma unroll 4
+        for (int c = t; c < BM * CPR; c += T::THREADS) {
+          const int row = c / CPR, cc = c - row * CPR;
+          const int m = m0 + row, n = n0 + cc * 8;
+          bool ok = m < rows_valid && n < p.N;
+          if (LAYOUT == kContiguous && ok) ok = p.m_indices[m] == g;
+          if (ok) {
+            const i32x4 v = *(const __attribute__((address_space(3))) i32x4*)(lds + row * ROWB + cc * 16);
+            *(i32x4*)(Dg + (size_t)m * p.N + n) = v;
+          }
+        }
+      }
+      TileDesc nx;
+      if (!next_tile(nx)) break;
+      wait_vm<0>();        // this tile's stores and LDS reads are done
+      wait_lgkm0();
+      block_barrier();
+      cur = nx;
+      setup(cur);
+      prologue();
     }
   }
-  wait_lgkm0();
-  block_barrier();
-  constexpr int CPR = BN * 2 / 16;   // 16-byte pieces per output row
-#pragma unroll 4
-  for (int c = t; c < BM * CPR; c += T::THREADS) {
-    const int row = c / CPR, cc = c - row * CPR;
-    const int m = m0 + row, n = n0 + cc * 8;
-    bool ok = m < rows_valid && n < p.N;
-    if (LAYOUT == kContiguous && ok) ok = p.m_indices[m] == g;
-    if (ok) {
-      const i32x4 v = *(const __attribute__((address_space(3))) i32x4*)(lds + row * ROWB + cc * 16);
-      *(i32x4*)(Dg + (size_t)m * p.N + n) = v;
-    }
-  }
+}
+
+// A single tile (see gemm_tiles).
+template <int LAYOUT, class T, bool POW2, int EPI>
+__device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, int g, const int m0,
+                                          const int n0, const int rows_valid, const int kb0 = 0,
+                                          int nkb = 0) {
+  bool done = false;
+  gemm_tiles<LAYOUT, T, POW2, EPI>(
+      p, lds,
+      [&](TileDesc& d) {
+        if (done) return false;
+        d = TileDesc{g, m0, n0, rows_valid};
+        done = true;
+        return true;
+      },
+      kb0, nkb);
 }
 
 // Contiguous layout with 256-row tiles. Experts' row segments are padded only
@@ -1019,17 +1156,16 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
     contiguous_run_tiles<T::THREADS, false>(p, (int*)smem, list, &s_group);
     const int ntm = s_group;
     const int total = ntm * p.tiles_n;
-    for (int tile = pos; tile < total; tile += gridDim.x) {
-      if (tile != pos) {   // the previous tile's epilogue is done with LDS
-        wait_vm<0>();
-        wait_lgkm0();
-        block_barrier();
-      }
+    int tile = pos;
+    gemm_tiles<LAYOUT, T, POW2, EPI>(p, lds, [&](TileDesc& d) {
+      if (tile >= total) return false;
       int mb, nbk;
       raster(tile, ntm, p.tiles_n, mb, nbk);
       const int e = list[mb];
-      gemm_tile<LAYOUT, T, POW2, EPI>(p, lds, e >> 16, (e & 0xffff) * 128, nbk * BN, p.M);
-    }
+      d = TileDesc{e >> 16, (e & 0xffff) * 128, nbk * BN, p.M};
+      tile += gridDim.x;
+      return true;
+    });
   } else {
     int tile = pos;
     int g = 0;
@@ -1070,24 +1206,39 @@ __global__ __launch_bounds__(T::THREADS) void fp8_bs_gemm(Params p) {
 // zwzgs.cn DeepGEMM page describes under "non-standard block sizes") puts
 // columns [0, n_split) on TA tiles -- tiles_a of them, whole rounds over the
 // CUs -- and the remaining columns on the narrower TB tiles, which fill the
-// last round. Workgroups [0, tiles_a) take TA tiles, the rest TB tiles; both
-// groups are XCD-grouped and rasterised like the single-shape kernel.
+// last round. The workgroups (one per CU) walk the TA tiles persistently, then
+// the TB tiles; tile i of either kind goes to workgroup i mod grid, and the
+// tiles are XCD-grouped and rasterised like the single-shape kernel's.
 template <class TA, class TB, bool POW2>
 __global__ __launch_bounds__(TA::THREADS) void fp8_bs_gemm_split(Params p) {
   static_assert(TA::THREADS == TB::THREADS, "both tile shapes run with the same workgroup size");
   constexpr int LDS = TA::LDS_BYTES > TB::LDS_BYTES ? TA::LDS_BYTES : TB::LDS_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
   lds_u8* const lds = (lds_u8*)smem;
-  const int b = blockIdx.x, na = p.tiles_a;
-  int mb, nbk;
-  if (b < na) {
-    raster(xcd_position(b, na), (p.M + TA::BM - 1) / TA::BM, p.n_split / TA::BN, mb, nbk);
-    gemm_tile<kDense, TA, POW2, kEpiBf16>(p, lds, 0, mb * TA::BM, nbk * TA::BN, p.M);
-  } else {
-    raster(xcd_position(b - na, gridDim.x - na), (p.M + TB::BM - 1) / TB::BM,
-           (p.N - p.n_split + TB::BN - 1) / TB::BN, mb, nbk);
-    gemm_tile<kDense, TB, POW2, kEpiBf16>(p, lds, 0, mb * TB::BM, p.n_split + nbk * TB::BN, p.M);
-  }
+  const int grid = gridDim.x, na = p.tiles_a;
+  const int tma = (p.M + TA::BM - 1) / TA::BM, tna = p.n_split / TA::BN;
+  const int tmb = (p.M + TB::BM - 1) / TB::BM, tnb = (p.N - p.n_split + TB::BN - 1) / TB::BN;
+  const int nb = tmb * tnb;
+  int k = blockIdx.x;
+  gemm_tiles<kDense, TA, POW2, kEpiBf16>(p, lds, [&](TileDesc& d) {
+    if (k >= na) return false;
+    int mb, nbk;
+    raster(xcd_position(k, na), tma, tna, mb, nbk);
+    d = TileDesc{0, mb * TA::BM, nbk * TA::BN, p.M};
+    k += grid;
+    return true;
+  });
+  wait_lgkm0();
+  block_barrier();   // no wave still reads the TA ring when the TB tiles' DMAs start
+  k = blockIdx.x;
+  gemm_tiles<kDense, TB, POW2, kEpiBf16>(p, lds, [&](TileDesc& d) {
+    if (k >= nb) return false;
+    int mb, nbk;
+    raster(xcd_position(k, nb), tmb, tnb, mb, nbk);
+    d = TileDesc{0, mb * TB::BM, p.n_split + nbk * TB::BN, p.M};
+    k += grid;
+    return true;
+  });
 }
 
 // Contiguous layout on run-following 256-row tiles (TF, 256 x BN) with the
@@ -1123,33 +1274,35 @@ __global__ __launch_bounds__(TF::THREADS) void fp8_bs_gemm_runs(Params p) {
   }
   const long halves = 2 * (full_items - whole);
   const long items = whole + halves + (long)S * tn;
-  const long pos = xcd_position(blockIdx.x, gridDim.x);
-  for (long w = pos; w < items; w += grid) {
-    if (w != pos) {   // the previous tile's epilogue is done with LDS
-      wait_vm<0>();
-      wait_lgkm0();
-      block_barrier();
-    }
+  long w = xcd_position(blockIdx.x, gridDim.x);
+  gemm_tiles<kContiguous, TF, POW2, EPI>(p, lds, [&](TileDesc& d) {
+    if (w >= whole) return false;
     int mb, nbk;
-    if (w < whole) {
-      raster((int)w, F, tn, mb, nbk);
-      const int e = list[mb];
-      gemm_tile<kContiguous, TF, POW2, EPI>(p, lds, e >> 16, (e & 0xffff) * 128, nbk * TF::BN, p.M);
-    } else {
-      const long h = w - whole;
-      int e, m0;
-      if (h < halves) {   // one 128-row half of a two-block tile
-        raster((int)(whole + h / 2), F, tn, mb, nbk);
-        e = list[mb];
-        m0 = (e & 0xffff) * 128 + (int)(h & 1) * 128;
-      } else {            // a single-block tile
-        raster((int)(h - halves), S, tn, mb, nbk);
-        e = list[kRunMaxBlocks - 1 - mb];
-        m0 = (e & 0xffff) * 128;
-      }
-      gemm_tile<kContiguous, TH, POW2, EPI>(p, lds, e >> 16, m0, nbk * TH::BN, p.M);
+    raster((int)w, F, tn, mb, nbk);
+    const int e = list[mb];
+    d = TileDesc{e >> 16, (e & 0xffff) * 128, nbk * TF::BN, p.M};
+    w += grid;
+    return true;
+  });
+  wait_lgkm0();
+  block_barrier();   // no wave still reads LDS of the 256-row tiles when the 128-row ones start
+  gemm_tiles<kContiguous, TH, POW2, EPI>(p, lds, [&](TileDesc& d) {
+    if (w >= items) return false;
+    const long h = w - whole;
+    int mb, nbk, e, m0;
+    if (h < halves) {   // one 128-row half of a two-block tile
+      raster((int)(whole + h / 2), F, tn, mb, nbk);
+      e = list[mb];
+      m0 = (e & 0xffff) * 128 + (int)(h & 1) * 128;
+    } else {            // a single-block tile
+      raster((int)(h - halves), S, tn, mb, nbk);
+      e = list[kRunMaxBlocks - 1 - mb];
+      m0 = (e & 0xffff) * 128;
     }
-  }
+    d = TileDesc{e >> 16, m0, nbk * TH::BN, p.M};
+    w += grid;
+    return true;
+  });
 }
 
 }  // namespace fg

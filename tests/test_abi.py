@@ -172,8 +172,8 @@ def test_select_config_fills_the_machine():
             assert grid == min(most, 256)
         elif (layout, M, N) == (0, 8192, 7168):
             # 3.5 rounds of 256x256 tiles: the two-shape split (3 whole rounds
-            # of 256x256 plus one round of 256x128)
-            assert (bm, bn) == (256, 256) and grid == 768 + 256
+            # of 256x256 plus one round of 256x128), walked by one workgroup per CU
+            assert (bm, bn) == (256, 256) and grid == 256
         else:
             assert grid == tiles
         if layout == 1:
@@ -198,9 +198,10 @@ def test_dense_split_chosen_for_partial_rounds():
     """The large dense FFN shape (32 x 28 tiles of 256x256 = 3.5 rounds over
     256 CUs) runs on the two-shape kernel: 24 column tiles of 256x256 (3 whole
     rounds) and the remaining 1024 columns as one round of 256x128 tiles. The
-    wide tile is the one reported; the grid counts both shapes."""
+    wide tile is the one reported; one workgroup per CU walks its tiles of
+    both shapes (fewer if there are fewer tiles of either shape)."""
     assert fg.select_config(8192, 7168, 18432, 1, 0) == (256, 256)
-    assert fg.select_grid(8192, 7168, 18432, 1, 0) == 768 + 256
+    assert fg.select_grid(8192, 7168, 18432, 1, 0) == 256
     # a problem already in whole rounds keeps the single shape
     assert fg.select_grid(8192, 4096, 7168, 1, 0) == 512
     # not for the fused epilogue (256-column tiles only) or the grouped layouts
