@@ -172,6 +172,7 @@ Plan split_plan(int M, int N, int nc, int cus) {
 
 #ifdef FG_TESTING
 thread_local int t_forced_split = -1;   // test build: force the dense split at this column
+thread_local int t_forced_grid = 0;     // test build: cap on the workgroups of the tile-walking kernels
 thread_local bool t_forced_runs = false;   // test build: force the contiguous runs kernel
 #endif
 
@@ -289,7 +290,6 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sa, 4) || !aligned(sb, 4)) return FG_EINVAL;
   if (m_indices && !aligned(m_indices, 4)) return FG_EINVAL;
   if (masked_m && !aligned(masked_m, 4)) return FG_EINVAL;
-  // the kernels address one expert's A or B with 32-bit byte offsets
   // 32-bit byte offsets: operand rows (M x K, N x K per expert) and the output
   // rows of one 256-row tile (256 x N bf16)
   if ((long long)M * K > 0x7fffffffLL || (long long)N * K > 0x7fffffffLL || N > kMaxN) return FG_EINVAL;
@@ -323,7 +323,13 @@ int run(int layout, const void* A, const float* sa, const void* B, const float* 
   p.n_split = plan.n_split;
   p.tiles_a = (int)plan.tiles_a;
   if (plan.grid > 0x7fffffffL) return FG_EINVAL;
-  const int grid = (int)plan.grid;
+  int grid = (int)plan.grid;
+#ifdef FG_TESTING
+  // the kernels whose workgroups walk their tiles cover every tile with any
+  // number of workgroups
+  if (t_forced_grid > 0 && (plan.split || plan.runs || run_path(layout, t)) && grid > t_forced_grid)
+    grid = t_forced_grid;
+#endif
 
   hipError_t e;
   if (fused)
@@ -475,6 +481,16 @@ int fgt_force_split(int n_split) {
   t_forced_tile = -1;
   t_forced_runs = false;
   t_forced_split = n_split;
+  return FG_OK;
+}
+
+// Test build only: launch at most `grid` workgroups for this thread's later
+// calls on the kernels whose workgroups walk their tiles (the dense two-shape
+// kernel, the contiguous 256-row kernels), so that each workgroup walks many
+// tiles; 0 restores the automatic grid. Other calls are unaffected.
+int fgt_force_grid(int grid) {
+  if (grid < 0) return FG_EINVAL;
+  t_forced_grid = grid;
   return FG_OK;
 }
 

@@ -9,6 +9,7 @@ built with FG_TESTING, which adds
     int fgt_force_tile(int bm, int bn);   /* per calling thread; 0, 0 = automatic */
     int fgt_force_split(int n_split);     /* dense on the two-shape kernel; -1 = automatic */
     int fgt_force_runs(int on);           /* contiguous on the runs kernel; 0 = automatic */
+    int fgt_force_grid(int grid);         /* cap on the tile-walking kernels' workgroups; 0 = automatic */
 
 ``forced_tile(bm, bn)`` routes the package's calls through that library for the
 duration of a ``with`` block (on this thread's override) and restores the
@@ -34,6 +35,8 @@ def testing_lib():
         L.fgt_force_split.restype = ctypes.c_int
         L.fgt_force_runs.argtypes = [ctypes.c_int]
         L.fgt_force_runs.restype = ctypes.c_int
+        L.fgt_force_grid.argtypes = [ctypes.c_int]
+        L.fgt_force_grid.restype = ctypes.c_int
         _tlib = L
     return _tlib
 
@@ -86,3 +89,17 @@ def forced_runs():
     finally:
         fg._lib = saved
         L.fgt_force_runs(0)
+
+
+@contextlib.contextmanager
+def forced_grid(grid):
+    """Inside the block (and inside a forced_* block of this module), launch at
+    most `grid` workgroups on the kernels whose workgroups walk their tiles."""
+    L = testing_lib()
+    rc = L.fgt_force_grid(grid)
+    if rc != 0:
+        raise fg.FGError(f"fgt_force_grid({grid}): {fg.strerror(rc)}")
+    try:
+        yield
+    finally:
+        L.fgt_force_grid(0)
