@@ -260,9 +260,14 @@ __device__ __forceinline__ void block_barrier() {
 // hardware range check keeps every load inside the operand), a loop-invariant
 // per-lane offset and one scalar offset per K-block. M0 holds the wave-uniform
 // LDS destination; one wait state separates its write from the DMA.
+// (A resource is uniform over the wave; readfirstlane states it for the
+// compiler, which keeps the resource in scalar registers as the instructions
+// need.)
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
-  return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)bytes, 0x20000};
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+               __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x20000};
 }
 template <int IMM>
 __device__ __forceinline__ void dma16(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t lds_at) {
@@ -531,32 +536,80 @@ __device__ __forceinline__ void gemm_tiles(const Params& p, lds_u8* const lds, N
   TileDesc cur;
   if (!next_tile(cur)) return;
 
-  // ---- per-tile DMA sources: a buffer resource per operand and per-lane
-  // byte offsets within one K-block column. Slot s of a tile region is the
-  // 16-byte LDS chunk s; it holds row s/8, chunk position s%8, i.e. global
-  // chunk (s%8) ^ (row%8). Rows that have no output -- padding slots past the
-  // tile, A rows past M, masked rows at or beyond masked_m[g], contiguous rows
-  // of padding or of another expert, B rows past N -- get the offset kNoRow,
-  // beyond the operand's buffer: the range check returns zeros for them
-  // without a memory access, so they cost no traffic and their MFMAs multiply
-  // zeros (the matrix core draws less power on them).
-  i32x4 rsA, rsB, rsS[T::SC_INSTR];
-  uint32_t a_off[T::A_INSTR], b_off[T::B_INSTR], sc_off[T::SC_INSTR];
+  // ---- DMA sources. Each tile gets a buffer resource per operand whose base
+  // is the tile's first row (A, B) or first scale (sa, sb) and whose size
+  // ends at the tile's last row with an output (A: rows_valid, B: N); the
+  // per-lane byte offsets within one K-block column are then the same for
+  // every tile. Slot s of a tile region is the 16-byte LDS chunk s; it holds
+  // row s/8, chunk position s%8, i.e. global chunk (s%8) ^ (row%8). Rows that
+  // have no output -- padding slots past the tile, A rows past M, masked rows
+  // at or beyond masked_m[g], contiguous rows of padding or of another
+  // expert, B rows past N -- fall past the resource's end (or get the offset
+  // kNoRow): the range check returns zeros for them without a memory access,
+  // so they cost no traffic and their MFMAs multiply zeros (the matrix core
+  // draws less power on them).
+  constexpr int NA = T::A_INSTR, NSC = T::SC_INSTR, NB = T::B_INSTR;
+  struct Srd {
+    i32x4 a, b, s[NSC];
+  };
+  uint32_t a_off[NA], b_off[NB], sc_off[NSC];
   int nb_lo, nb_hi, j_switch;
   // Scale loads: load i = q*W + wave brings activation rows [64i, 64i+64)
   // (i < BM/64) or the weight scales of the tile's 128-column blocks
-  // (i == BM/64, clamped); a wave without a load of its own repeats load 0.
-  int sc_row[T::SC_INSTR];   // i * 64, or -1 for the weight-scale load
-  uint32_t sc_stride[T::SC_INSTR], sc_dst[T::SC_INSTR];
+  // (i == BM/64); a wave without a load of its own repeats load 0.
+  int sc_row[NSC];   // i * 64, or -1 for the weight-scale load
+  uint32_t sc_stride[NSC], sc_dst[NSC];
 #pragma unroll
-  for (int q = 0; q < T::SC_INSTR; ++q) {
+  for (int q = 0; q < NSC; ++q) {
     int i = q * W + wave;
     if (i >= T::SC_LOADS) i = 0;
     const bool is_b = i == BM / 64;
     sc_row[q] = is_b ? -1 : i * 64;
     sc_stride[q] = is_b ? 4u : (uint32_t)M * 4u;
     sc_dst[q] = lds_addr + T::SC_BASE + (is_b ? BM * 4 : i * 256);
+    // weight scales: a tile reads at most the blocks nb_tile .. nb_tile+2, so
+    // lanes past 3 repeat lane 3's row (one cache line instead of one per lane)
+    sc_off[q] = is_b ? (uint32_t)min(lane, 3) * (uint32_t)KB * 4u : (uint32_t)(i * 64 + lane) * 4u;
   }
+  auto a_slot = [&](int q, int& row, int& chunk) {
+    const int slot = (q * W + wave) * 64 + lane;
+    row = slot >> 3;
+    chunk = (slot & 7) ^ (row & 7);
+  };
+#pragma unroll
+  for (int q = 0; q < NA; ++q) {
+    int row, chunk;
+    a_slot(q, row, chunk);
+    a_off[q] = row < BM ? (uint32_t)row * (uint32_t)K + chunk * 16 : kNoRow;
+  }
+#pragma unroll
+  for (int q = 0; q < NB; ++q) {
+    const int slot = (q * W + wave) * 64 + lane;
+    const int row = slot >> 3, chunk = (slot & 7) ^ (row & 7);
+    b_off[q] = row < BN ? (uint32_t)(DIRECT ? pair_column(row) : row) * (uint32_t)K + chunk * 16 : kNoRow;
+  }
+  // the buffer resources of tile d (sizes clamp at 0: a tile past every row
+  // with an output reads zeros only)
+  auto srd_of = [&](const TileDesc& d) {
+    const int g = d.g, m0 = d.m0, n0 = d.n0;
+    const uint8_t* Ag = p.A + (LAYOUT == kMasked ? (size_t)g * M * K : 0);
+    const float* sag = p.sa + (LAYOUT == kMasked ? (size_t)g * KB * M : 0);
+    const uint8_t* Bg = p.B + (LAYOUT != kDense ? (size_t)g * p.N * K : 0);
+    const float* sbg = p.sb + (LAYOUT != kDense ? (size_t)g * NB128 * KB : 0);
+    const int rows = max(0, min(d.rows_valid - m0, BM)), cols = max(0, min(p.N - n0, BN));
+    const int nb_tile = n0 >> 7;
+    Srd r;
+    r.a = buffer_rsrc(Ag + (size_t)m0 * K, (uint32_t)rows * (uint32_t)K);
+    r.b = buffer_rsrc(Bg + (size_t)n0 * K, (uint32_t)cols * (uint32_t)K);
+    // activation scales: rows past M read the next K-block's first rows (or
+    // zeros past the end); those rows have no output
+    const i32x4 rsSA = buffer_rsrc(sag + m0, (uint32_t)(KB * M - m0) * 4u);
+    const i32x4 rsSB = buffer_rsrc(sbg + (size_t)nb_tile * KB, (uint32_t)(NB128 - nb_tile) * (uint32_t)KB * 4u);
+#pragma unroll
+    for (int q = 0; q < NSC; ++q) r.s[q] = sc_row[q] < 0 ? rsSB : rsSA;
+    return r;
+  };
+  Srd rs;   // this tile's resources
   // ---- per-lane LDS addresses of this wave's fragments and scales. Chunk c
   // of tile row r sits at r*128 + ((c ^ (r & 7)) << 4); a wave's fragments
   // start at multiples of 16 rows, so r & 7 == lr & 7 and every fragment is
@@ -573,43 +626,22 @@ __device__ __forceinline__ void gemm_tiles(const Params& p, lds_u8* const lds, N
     sA.init(lds_addr + (wm * WM + lr) * 4);
   }
   auto setup = [&](const TileDesc& d) {
-    const int g = d.g, m0 = d.m0, n0 = d.n0, rows_valid = d.rows_valid;
-    const uint8_t* Ag = p.A + (LAYOUT == kMasked ? (size_t)g * M * K : 0);
-    const float* sag = p.sa + (LAYOUT == kMasked ? (size_t)g * KB * M : 0);
-    const uint8_t* Bg = p.B + (LAYOUT != kDense ? (size_t)g * p.N * K : 0);
-    const float* sbg = p.sb + (LAYOUT != kDense ? (size_t)g * NB128 * KB : 0);
-    rsA = buffer_rsrc(Ag, (uint32_t)M * (uint32_t)K);
-    rsB = buffer_rsrc(Bg, (uint32_t)p.N * (uint32_t)K);
+    const int g = d.g, m0 = d.m0, n0 = d.n0;
+    rs = srd_of(d);
+    if constexpr (LAYOUT == kContiguous) {
+      // rows of padding or of another expert load nothing
 #pragma unroll
-    for (int q = 0; q < T::A_INSTR; ++q) {
-      const int slot = (q * W + wave) * 64 + lane;
-      const int row = slot >> 3, chunk = (slot & 7) ^ (row & 7);
-      const int m = m0 + row;
-      bool live = row < BM && m < rows_valid;
-      if (LAYOUT == kContiguous && live) live = p.m_indices[m] == g;
-      a_off[q] = live ? (uint32_t)m * (uint32_t)K + chunk * 16 : kNoRow;
-    }
-#pragma unroll
-    for (int q = 0; q < T::B_INSTR; ++q) {
-      const int slot = (q * W + wave) * 64 + lane;
-      const int row = slot >> 3, chunk = (slot & 7) ^ (row & 7);
-      const int n = n0 + (DIRECT ? pair_column(row) : row);
-      b_off[q] = row < BN && n < p.N ? (uint32_t)n * (uint32_t)K + chunk * 16 : kNoRow;
-    }
-    const int nb_tile = n0 >> 7;
-    const i32x4 rsSA = buffer_rsrc(sag, (uint32_t)KB * (uint32_t)M * 4u);
-    const i32x4 rsSB = buffer_rsrc(sbg, (uint32_t)NB128 * (uint32_t)KB * 4u);
-#pragma unroll
-    for (int q = 0; q < T::SC_INSTR; ++q) {
-      const bool is_b = sc_row[q] < 0;
-      rsS[q] = is_b ? rsSB : rsSA;
-      // weight scales: a tile reads at most the blocks nb_tile .. nb_tile+2, so
-      // lanes past 3 repeat lane 3's row (one cache line instead of one per lane)
-      sc_off[q] = is_b ? (uint32_t)min(nb_tile + min(lane, 3), NB128 - 1) * (uint32_t)KB * 4u
-                       : (uint32_t)min(m0 + sc_row[q] + lane, M - 1) * 4u;
+      for (int q = 0; q < NA; ++q) {
+        int row, chunk;
+        a_slot(q, row, chunk);
+        const int m = m0 + row;
+        const bool live = row < BM && m < M && p.m_indices[m] == g;
+        a_off[q] = live ? (uint32_t)row * (uint32_t)K + chunk * 16 : kNoRow;
+      }
     }
     // scale blocks of B covered by this wave's columns (at most two) and the
     // first sub-tile column whose scale block is nb_hi
+    const int nb_tile = n0 >> 7;
     const int wn0 = n0 + wn * WN;
     nb_lo = uniform(min(wn0 >> 7, NB128 - 1));
     nb_hi = uniform(min(nb_lo + 1, NB128 - 1));
@@ -631,19 +663,18 @@ __device__ __forceinline__ void gemm_tiles(const Params& p, lds_u8* const lds, N
     for (int q = 0; q < T::SC_INSTR; ++q) o.sc[q] = (uint32_t)(kb0 + ka) * sc_stride[q];
     return o;
   };
-  constexpr int NA = T::A_INSTR, NSC = T::SC_INSTR, NB = T::B_INSTR;
   // DMA instruction d of a group (A chunks, then scale loads, then B chunks)
-  // into A-ring stage AST and B-ring stage BST
-  auto issue = [&](auto d_c, auto ast_c, auto bst_c, const Soff& o) {
+  // of the tile with resources r into A-ring stage AST and B-ring stage BST
+  auto issue = [&](auto d_c, auto ast_c, auto bst_c, const Soff& o, const Srd& r) {
     constexpr int d = decltype(d_c)::value, AST = decltype(ast_c)::value, BST = decltype(bst_c)::value;
     if constexpr (d < NA) {
-      dma16<T::A_BASE + AST * T::A_BYTES + d * W * 1024>(rsA, a_off[d], o.a, wave_at);
+      dma16<T::A_BASE + AST * T::A_BYTES + d * W * 1024>(r.a, a_off[d], o.a, wave_at);
     } else if constexpr (d < NA + NSC) {
       constexpr int q = d - NA;
-      dma4<AST * T::SC_BYTES>(rsS[q], sc_off[q], o.sc[q], sc_dst[q]);
+      dma4<AST * T::SC_BYTES>(r.s[q], sc_off[q], o.sc[q], sc_dst[q]);
     } else {
       constexpr int q = d - NA - NSC;
-      dma16<T::B_BASE + BST * T::B_BYTES + q * W * 1024>(rsB, b_off[q], o.b, wave_at);
+      dma16<T::B_BASE + BST * T::B_BYTES + q * W * 1024>(r.b, b_off[q], o.b, wave_at);
     }
   };
 
@@ -698,7 +729,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& p, lds_u8* const lds, N
       static_for<2>([&](auto x_c) {
         constexpr int x = decltype(x_c)::value;
         const Soff o = soff_of(min(x, nkb - 1), min(x, nkb - 1));
-        static_for<D>([&](auto d_c) { issue(d_c, x_c, x_c, o); });
+        static_for<D>([&](auto d_c) { issue(d_c, x_c, x_c, o, rs); });
       });
     } else {
       static_for<SB>([&](auto x_c) {
@@ -709,7 +740,7 @@ __device__ __forceinline__ void gemm_tiles(const Params& p, lds_u8* const lds, N
           constexpr int d = decltype(d_c)::value;
           constexpr bool a_part = d < NA + NSC;
           if constexpr (!(a_part && ka < 0) && !(x == SB - 1 && SCH::slot(d) >= POST))
-            issue(d_c, std::integral_constant<int, (ka < 0 ? 0 : ka)>{}, x_c, o);
+            issue(d_c, std::integral_constant<int, (ka < 0 ? 0 : ka)>{}, x_c, o, rs);
         });
       });
     }
@@ -718,7 +749,8 @@ __device__ __forceinline__ void gemm_tiles(const Params& p, lds_u8* const lds, N
   static_assert(WAIT_PRO + NST < 64, "vmcnt counter range");
   setup(cur);
   prologue();
-  bool after_stores = false;   // the previous tile's NST stores were issued after this tile's prologue
+  TileDesc nx = cur;
+  bool after_stores = false;   // the previous tile's NST stores were issued after this tile's first loads
   for (;;) {
     if (after_stores) {
       wait_vm<WAIT_PRO + NST>();
@@ -884,11 +916,11 @@ __device__ __forceinline__ void gemm_tiles(const Params& p, lds_u8* const lds, N
         static_for<D>([&](auto d_c) {
           constexpr int d = decltype(d_c)::value;
           if constexpr (SPLIT) {
-            if constexpr (SCH::slot(d) == u) issue(d_c, CurA{}, CurB{}, head);   // K-block kb+2
+            if constexpr (SCH::slot(d) == u) issue(d_c, CurA{}, CurB{}, head, rs);   // K-block kb+2
           } else {
-            if constexpr (u >= PRE && SCH::slot(d) == u - PRE) issue(d_c, CurA{}, CurB{}, head);
+            if constexpr (u >= PRE && SCH::slot(d) == u - PRE) issue(d_c, CurA{}, CurB{}, head, rs);
             if constexpr (u < PRE && SCH::slot(d) == POST + u)
-              issue(d_c, std::integral_constant<int, TA>{}, std::integral_constant<int, TB>{}, tail);
+              issue(d_c, std::integral_constant<int, TA>{}, std::integral_constant<int, TB>{}, tail, rs);
           }
         });
         if constexpr (!POW2) promote_step(ph_c, u_c);
@@ -949,7 +981,6 @@ __device__ __forceinline__ void gemm_tiles(const Params& p, lds_u8* const lds, N
         // in flight (a later wait for it would also wait for them)
         asm volatile("" : "+v"(roff[i]));
       }
-      TileDesc nx;
       const bool more = next_tile(nx);
       if (more) {
         setup(nx);
@@ -1005,7 +1036,6 @@ __device__ __forceinline__ void gemm_tiles(const Params& p, lds_u8* const lds, N
           }
         }
       }
-      TileDesc nx;
       if (!next_tile(nx)) break;
       wait_vm<0>();        // this tile's stores and LDS reads are done
       wait_lgkm0();
