@@ -1100,22 +1100,32 @@ __device__ __forceinline__ void contiguous_run_tiles(const Params& p, int* blk, 
   const int nblk = (p.M + 127) / 128;
   constexpr int BPI = THREADS / 32;   // blocks per pass-1 iteration
   const int iters = (nblk + BPI - 1) / BPI;
-  for (int it = 0; it < iters; ++it) {   // same trip count for every lane (shuffles below)
-    const int bk = it * BPI + (t >> 5), h = t & 31;
-    int v = -1;
-    if (bk < nblk) {
+  // Lane h of a block's 32 reads rows 4h .. 4h+3 (one 16-byte load through a
+  // buffer resource over m_indices: rows past M read zeros, masked below);
+  // the loads of BATCH iterations are in flight together.
+  constexpr int BATCH = 8;
+  const __amdgpu_buffer_rsrc_t rsI =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.m_indices, 0, p.M * 4, 0x20000);
+  for (int it0 = 0; it0 < iters; it0 += BATCH) {   // same trip counts for every lane (shuffles below)
+    i32x4 ids[BATCH];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = bk * 128 + r * 32 + h;
-        if (m < p.M) {
-          const int id = p.m_indices[m];
-          if (id >= 0 && id < p.G) v = max(v, id);
-        }
-      }
+    for (int b = 0; b < BATCH; ++b) {
+      const int bk = (it0 + b) * BPI + (t >> 5), h = t & 31;
+      ids[b] = __builtin_amdgcn_raw_buffer_load_b128(rsI, (uint32_t)(bk * 128 + h * 4) * 4u, 0, 0);
     }
 #pragma unroll
-    for (int d = 16; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, 32));
-    if (h == 0 && bk < nblk) blk[bk] = v;
+    for (int b = 0; b < BATCH; ++b) {
+      const int bk = (it0 + b) * BPI + (t >> 5), h = t & 31;
+      int v = -1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = bk * 128 + h * 4 + r, id = ids[b][r];
+        if (m < p.M && id >= 0 && id < p.G) v = max(v, id);
+      }
+#pragma unroll
+      for (int d = 16; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, 32));
+      if (h == 0 && bk < nblk) blk[bk] = v;
+    }
   }
   __syncthreads();
   if (t < 64) {
