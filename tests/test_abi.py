@@ -58,6 +58,7 @@ GOOD = ctypes.c_void_p(0x100000)   # aligned, never dereferenced (validation fai
     (BAD, GOOD, GOOD, GOOD, GOOD, 64, 256, 256, None),        # misaligned A
     (GOOD, GOOD, GOOD, GOOD, BAD, 64, 256, 256, None),        # misaligned D
     (GOOD, GOOD, GOOD, GOOD, GOOD, 1 << 20, 256, 4096, None),  # M*K beyond 2^31
+    (GOOD, GOOD, GOOD, GOOD, GOOD, 64, 4194304, 128, None),    # N beyond 4194296 (a 256-row tile of D past 2^31 bytes)
 ])
 def test_dense_validation(args):
     assert fg.lib().fg_gemm_fp8_nt(*args) == EINVAL
