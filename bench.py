@@ -41,7 +41,11 @@ same calls on a single input copy, resident in the MALL where it fits
 (reported beside the cold numbers, never as `value`). `mfma_ceiling` is what
 the matrix cores sustain on this device for the GEMM's inner loop with no
 memory traffic (random and all-zero E4M3 codes), and roofline
-`frac_of_measured_mfma_ceiling` the headline kernel against it.
+`frac_of_measured_mfma_ceiling` the headline kernel against it;
+`hbm_read_ceiling` is what a plain streaming read (16-byte nontemporal loads,
+8 in flight per thread, 8 workgroups of 512 threads per CU) pulls from HBM on
+this device, and each HBM-bound workload's `frac_of_measured_hbm_read` its
+algorithmic bytes per second against that.
 """
 import argparse
 import ctypes
@@ -429,6 +433,40 @@ def mfma_ceiling(torch, warmup_ms):
     return res
 
 
+def hbm_read_ceiling(torch, warmup_ms, mb=1024):
+    """HBM bytes per second a plain streaming read sustains on this device
+    (libfg_ceiling.so's fgc_stream_read over a buffer 4x the MALL's size)."""
+    L = ctypes.CDLL(os.path.join(ROOT, "moe_grouped_gemm_02_amd", "libfg_ceiling.so"))
+    L.fgc_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.fgc_stream_read.restype = ctypes.c_int
+    nbytes = mb << 20
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    grid = torch.cuda.get_device_properties(0).multi_processor_count * 8
+    out = torch.empty(grid * 512, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch():
+        if L.fgc_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()), grid,
+                             stream) != 0:
+            raise RuntimeError("fgc_stream_read failed")
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < warmup_ms:
+        launch()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"gb_s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBPS, 4), "bytes": nbytes,
+            "workgroups": grid}
+
+
 def kernel_source_hash():
     """Hash of what defines the kernels: the kernel template with comments and
     whitespace removed, and the tile-configuration lines that instantiate it.
@@ -624,12 +662,20 @@ def main():
     if args.calibrate_copy_mb:
         copy_calibration(args.calibrate_copy_mb, torch)
     roof["traffic"] = measured_traffic(args.workload) if not head_pow2 else None
-    ceiling = None
+    ceiling = hbm_ceiling = None
     if full:
         ceiling = mfma_ceiling(torch, args.warmup_ms)
+        hbm_ceiling = hbm_read_ceiling(torch, args.warmup_ms)
         if not hbm_bound:
             key = "random_pow2" if head_pow2 else "random_fp32_promotion"
             roof["frac_of_measured_mfma_ceiling"] = round(achieved_tflops / ceiling[key]["tflops"], 4)
+        else:
+            roof["frac_of_measured_hbm_read"] = round(achieved_gbps / hbm_ceiling["gb_s"], 4)
+        for table in (per, per_pow2):
+            for e in table.values():
+                # FLOP per algorithmic byte below the ridge point: HBM is the roof
+                if e["hbm_gbps"] > 0 and e["tflops"] * 1e3 / e["hbm_gbps"] < ridge:
+                    e["frac_of_measured_hbm_read"] = round(e["hbm_gbps"] / hbm_ceiling["gb_s"], 4)
 
     line = {
         "metric": "FP8 TFLOPS (dense + grouped MoE) and % of MI355X dense FP8 MFMA peak",
@@ -653,6 +699,7 @@ def main():
                    "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2)},
         "roofline": roof,
         "mfma_ceiling": ceiling,
+        "hbm_read_ceiling": hbm_ceiling,
         "cpu_baseline": cpu_cfg.get(args.workload),
         "cpu_baseline_per_config": cpu_cfg or None,
         "per_workload": per,

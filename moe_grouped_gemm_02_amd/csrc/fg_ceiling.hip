@@ -1,7 +1,8 @@
-// fg_ceiling.hip -- the matrix-core ceiling the GEMM's inner loop can reach on
-// this device: the GEMM's K-loop arithmetic with no memory traffic at all. A
-// benchmark helper (libfg_ceiling.so, loaded by bench.py only), not part of
-// the library.
+// fg_ceiling.hip -- what this device sustains for the two resources the GEMM
+// is bound by: the matrix-core ceiling of its inner loop (the K-loop
+// arithmetic with no memory traffic at all) and the practical HBM read rate (a
+// plain streaming read). A benchmark helper (libfg_ceiling.so, loaded by
+// bench.py only), not part of the library.
 //
 // Each workgroup has 8 waves (two per SIMD, as in the GEMM's 256-row tiles);
 // each wave holds 4 A and 8 B fragments of 16 rows x 128 E4M3 codes (a 64x128
@@ -21,6 +22,7 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kTM = 4, kTN = 8, kSteps = kTM * kTN;
 constexpr int kWordsPerWave = (kTM + kTN) * 8 * 64;   // fragments x 8 dwords x 64 lanes
 constexpr int kWaveSets = 64;                          // distinct fragment sets in src
@@ -77,6 +79,27 @@ __global__ __launch_bounds__(512) void mfma_loop(const int* __restrict__ src, fl
   out[blockIdx.x * 512 + threadIdx.x] = t;
 }
 
+// Streaming read of n 16-byte words: grid-stride, 8 nontemporal loads in
+// flight per thread, folded into one value per thread so nothing is dropped.
+__global__ __launch_bounds__(512) void stream_read(const i32x4* __restrict__ src, long n, int* __restrict__ out) {
+  constexpr int kUnroll = 8;
+  long i = (long)blockIdx.x * 512 + threadIdx.x;
+  const long stride = (long)gridDim.x * 512;
+  int acc = 0;
+  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+    i32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n; i += stride) {
+    const i32x4 v = src[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  out[(long)blockIdx.x * 512 + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,6 +118,15 @@ int fgc_mfma_loop(const int* src, float* out, int mode, int grid, int iters, hip
     hipLaunchKernelGGL(mfma_loop<0>, dim3(grid), dim3(512), 0, stream, src, out, iters, 0.5f);
   else
     hipLaunchKernelGGL(mfma_loop<1>, dim3(grid), dim3(512), 0, stream, src, out, iters, 0.5f);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// Reads `bytes` (a positive multiple of 16) of device memory at src (16-byte
+// aligned) with `grid` workgroups of 512 threads; out holds grid * 512 ints.
+// Returns 0, or -1 for a bad argument, -3 if the launch failed.
+int fgc_stream_read(const void* src, long bytes, int* out, int grid, hipStream_t stream) {
+  if (!src || !out || grid < 1 || bytes < 16 || bytes % 16 || ((uintptr_t)src & 15)) return -1;
+  hipLaunchKernelGGL(stream_read, dim3(grid), dim3(512), 0, stream, (const i32x4*)src, bytes / 16, out);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
