@@ -79,19 +79,19 @@ __global__ __launch_bounds__(512) void mfma_loop(const int* __restrict__ src, fl
   out[blockIdx.x * 512 + threadIdx.x] = t;
 }
 
-// Streaming read of n 16-byte words: grid-stride, 8 nontemporal loads in
+// Streaming read of n 16-byte words: grid-stride, UNR nontemporal loads in
 // flight per thread, folded into one value per thread so nothing is dropped.
+template <int UNR>
 __global__ __launch_bounds__(512) void stream_read(const i32x4* __restrict__ src, long n, int* __restrict__ out) {
-  constexpr int kUnroll = 8;
   long i = (long)blockIdx.x * 512 + threadIdx.x;
   const long stride = (long)gridDim.x * 512;
   int acc = 0;
-  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
-    i32x4 v[kUnroll];
+  for (; i + (UNR - 1) * stride < n; i += UNR * stride) {
+    i32x4 v[UNR];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < UNR; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    for (int u = 0; u < UNR; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   for (; i < n; i += stride) {
     const i32x4 v = src[i];
@@ -122,11 +122,17 @@ int fgc_mfma_loop(const int* src, float* out, int mode, int grid, int iters, hip
 }
 
 // Reads `bytes` (a positive multiple of 16) of device memory at src (16-byte
-// aligned) with `grid` workgroups of 512 threads; out holds grid * 512 ints.
+// aligned) with `grid` workgroups of 512 threads, each thread keeping
+// `inflight` (4 or 8) 16-byte loads in flight; out holds grid * 512 ints.
 // Returns 0, or -1 for a bad argument, -3 if the launch failed.
-int fgc_stream_read(const void* src, long bytes, int* out, int grid, hipStream_t stream) {
+int fgc_stream_read(const void* src, long bytes, int* out, int grid, int inflight, hipStream_t stream) {
   if (!src || !out || grid < 1 || bytes < 16 || bytes % 16 || ((uintptr_t)src & 15)) return -1;
-  hipLaunchKernelGGL(stream_read, dim3(grid), dim3(512), 0, stream, (const i32x4*)src, bytes / 16, out);
+  if (inflight == 4)
+    hipLaunchKernelGGL(stream_read<4>, dim3(grid), dim3(512), 0, stream, (const i32x4*)src, bytes / 16, out);
+  else if (inflight == 8)
+    hipLaunchKernelGGL(stream_read<8>, dim3(grid), dim3(512), 0, stream, (const i32x4*)src, bytes / 16, out);
+  else
+    return -1;
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -273,10 +273,12 @@ def test_ceiling_helper_loads():
     L = ctypes.CDLL(os.path.join(os.path.dirname(fg.LIB_PATH), "libfg_ceiling.so"), mode=os.RTLD_NOW)
     for name in ("fgc_src_words", "fgc_flop_per_workgroup_iteration", "fgc_mfma_loop", "fgc_stream_read"):
         assert hasattr(L, name), name
-    L.fgc_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    assert L.fgc_stream_read(None, 1 << 20, None, 1, None) == -1
-    assert L.fgc_stream_read(ctypes.c_void_p(0x1008), 1 << 20, ctypes.c_void_p(0x2000), 1, None) == -1   # misaligned
-    assert L.fgc_stream_read(ctypes.c_void_p(0x1000), 100, ctypes.c_void_p(0x2000), 1, None) == -1       # not whole 16 B
+    L.fgc_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    assert L.fgc_stream_read(None, 1 << 20, None, 1, 4, None) == -1
+    assert L.fgc_stream_read(ctypes.c_void_p(0x1008), 1 << 20, ctypes.c_void_p(0x2000), 1, 4, None) == -1  # misaligned
+    assert L.fgc_stream_read(ctypes.c_void_p(0x1000), 100, ctypes.c_void_p(0x2000), 1, 4, None) == -1      # not whole 16 B
+    assert L.fgc_stream_read(ctypes.c_void_p(0x1000), 1 << 20, ctypes.c_void_p(0x2000), 1, 5, None) == -1  # 4 or 8 in flight
     L.fgc_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_void_p]
     assert L.fgc_mfma_loop(None, None, 0, 1, 1, None) == -1        # rejected before any launch
