@@ -20,9 +20,11 @@
 // and scales go into one ring of LDS stages, B tiles into a second ring that
 // may run further ahead (B streams from HBM; A is re-read from L2 by every
 // N-tile). One workgroup barrier per K-block both publishes the next stage
-// and frees the stages just consumed. The barrier sits before the last
-// columns of MFMAs, so the next K-block's fragments are read from LDS while
-// those MFMAs run.
+// and frees the stages just consumed (two with a two-stage ring, which frees
+// its A half earlier). The barrier sits before the last columns of MFMAs, so
+// the next K-block's fragments are read from LDS while those MFMAs run. A
+// workgroup may compute several tiles one after another (gemm_tiles); each
+// tile addresses its operands through buffer resources of its own.
 //
 // LDS layout: the scale blocks of all A stages (BM activation scales and the
 // weight scales of the tile's 128-column blocks, fp32), then the A tiles
@@ -35,8 +37,9 @@
 // Operand roles. The MFMA's first operand is fed with rows of B (output
 // columns n), its second with rows of A (output rows m). The 16x16 result then
 // gives each lane four consecutive n for a single m, so a lane needs one
-// activation scale per sub-tile row and its four results form one 8-byte bf16
-// store.
+// activation scale per sub-tile row. Loading the B rows of two neighbouring
+// sub-tiles in pair_column order makes a lane's eight results of the pair
+// eight consecutive columns: one 16-byte bf16 store straight from registers.
 //
 // Fused epilogue (EPI = kEpiSwigluQuant), for an MoE expert's first
 // projection whose weight interleaves gate and up rows every 128: the 2kiu.com
