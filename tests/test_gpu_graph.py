@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import moe_grouped_gemm_02_amd as fg
-from fgtesting import forced_tile as forced
+from fgtesting import forced_grid, forced_runs, forced_split, forced_tile as forced
 from fgtest import (SENTINEL, d_bits, dense_inputs, make_contiguous, make_dense, make_masked,
                     masked_inputs, new_out, to_dev)
 
@@ -149,3 +149,31 @@ def test_graph_fused_and_quantiser():
     codes, scales = oracle.quantize_act_1x128(x.cpu().numpy())
     assert np.array_equal(eager[0], codes)
     assert np.array_equal(eager[1].view(np.float32).reshape(4, 96), scales.T)
+
+
+@pytest.mark.parametrize("kernel", ["split", "runs"])
+def test_graph_tile_walk(kernel):
+    """The kernels whose workgroups walk their tiles (dense two-shape, contiguous
+    runs), with few workgroups so each walks several tiles, captured and
+    replayed."""
+    print(f"graph tile walk {kernel}", flush=True)
+    if kernel == "split":
+        A, sa, B, sb = make_dense(1000, 1160, 640, 406)
+        Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
+        D, D2 = new_out((1000, 1160)), new_out((1000, 1160))
+        with forced_split(768), forced_grid(3):
+            replay_matches_eager(lambda o: fg.gemm_fp8_nt(Ad, sad, Bd, sbd, o[0]), [D],
+                                 lambda o: [fill_sentinel(x) for x in o], [D2])
+        r = oracle.check(d_bits(D), oracle.ref_dense(A, sa, B, sb))
+    else:
+        A, sa, B, sb, mi = make_contiguous(3, 512, 640, 407, m_lo=200, m_hi=700)
+        Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
+        mid = to_dev(mi)
+        M = A.shape[0]
+        D, D2 = new_out((M, 512)), new_out((M, 512))
+        with forced_runs(), forced_grid(2):
+            replay_matches_eager(lambda o: fg.grouped_contiguous(Ad, sad, Bd, sbd, o[0], mid), [D],
+                                 lambda o: [fill_sentinel(x) for x in o], [D2])
+        ref, valid = oracle.ref_contiguous(A, sa, B, sb, mi)
+        r = oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
+    assert r["ok"], r
