@@ -104,16 +104,29 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _fp8(t, name, shape):
+def _call(fn, dev, *args):
+    """Calls entry point `fn` with `dev` as the current device (the library
+    launches on the current device, on the stream passed last) and raises
+    FGError on a nonzero return code."""
+    torch = _torch()
+    with torch.cuda.device(dev):
+        _check(getattr(lib(), fn)(*args), fn)
+
+
+def _fp8(t, name, shape, device=None):
     torch = _torch()
     if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
         raise TypeError(f"{name} must be uint8 or float8_e4m3fn E4M3 bytes, got {t.dtype}")
-    _dev(t, name, shape)
+    _dev(t, name, shape, device=device)
 
 
-def _dev(t, name, shape, dtype=None):
+def _dev(t, name, shape, dtype=None, device=None):
+    """Checks a tensor argument: on a GPU (on `device` if given), of `dtype`
+    (if given), of `shape`, contiguous."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's operands on {device}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
@@ -141,15 +154,15 @@ def _dense(fn, A, sa, B, sb, D):
     torch = _torch()
     M, K = A.shape
     N = B.shape[0]
+    dev = A.device
     _fp8(A, "A", (M, K))
-    _fp8(B, "B", (N, K))
+    _fp8(B, "B", (N, K), dev)
     if K % 128 or N % 8:
         raise ValueError("K must be a multiple of 128 and N of 8")
-    _dev(sa, "sa", (K // 128, M), torch.float32)
-    _dev(sb, "sb", (-(-N // 128), K // 128), torch.float32)
-    _dev(D, "D", (M, N), torch.bfloat16)
-    _check(getattr(lib(), fn)(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D), M, N, K,
-                              _stream(A)), fn)
+    _dev(sa, "sa", (K // 128, M), torch.float32, dev)
+    _dev(sb, "sb", (-(-N // 128), K // 128), torch.float32, dev)
+    _dev(D, "D", (M, N), torch.bfloat16, dev)
+    _call(fn, dev, _ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D), M, N, K, _stream(A))
     return D
 
 
@@ -168,16 +181,16 @@ def _contiguous(fn, A, sa, B, sb, D, m_indices):
     torch = _torch()
     M, K = A.shape
     G, N = B.shape[0], B.shape[1]
+    dev = A.device
     _fp8(A, "A", (M, K))
-    _fp8(B, "B", (G, N, K))
+    _fp8(B, "B", (G, N, K), dev)
     if K % 128 or N % 8:
         raise ValueError("K must be a multiple of 128 and N of 8")
-    _dev(sa, "sa", (K // 128, M), torch.float32)
-    _dev(sb, "sb", (G, -(-N // 128), K // 128), torch.float32)
-    _dev(D, "D", (M, N), torch.bfloat16)
-    _dev(m_indices, "m_indices", (M,), torch.int32)
-    _check(getattr(lib(), fn)(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D),
-                              _ptr(m_indices), M, N, K, G, _stream(A)), fn)
+    _dev(sa, "sa", (K // 128, M), torch.float32, dev)
+    _dev(sb, "sb", (G, -(-N // 128), K // 128), torch.float32, dev)
+    _dev(D, "D", (M, N), torch.bfloat16, dev)
+    _dev(m_indices, "m_indices", (M,), torch.int32, dev)
+    _call(fn, dev, _ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D), _ptr(m_indices), M, N, K, G, _stream(A))
     return D
 
 
@@ -196,16 +209,16 @@ def _masked(fn, A, sa, B, sb, D, masked_m):
     torch = _torch()
     G, M_max, K = A.shape
     N = B.shape[1]
+    dev = A.device
     _fp8(A, "A", (G, M_max, K))
-    _fp8(B, "B", (G, N, K))
+    _fp8(B, "B", (G, N, K), dev)
     if K % 128 or N % 8:
         raise ValueError("K must be a multiple of 128 and N of 8")
-    _dev(sa, "sa", (G, K // 128, M_max), torch.float32)
-    _dev(sb, "sb", (G, -(-N // 128), K // 128), torch.float32)
-    _dev(D, "D", (G, M_max, N), torch.bfloat16)
-    _dev(masked_m, "masked_m", (G,), torch.int32)
-    _check(getattr(lib(), fn)(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D),
-                              _ptr(masked_m), G, M_max, N, K, _stream(A)), fn)
+    _dev(sa, "sa", (G, K // 128, M_max), torch.float32, dev)
+    _dev(sb, "sb", (G, -(-N // 128), K // 128), torch.float32, dev)
+    _dev(D, "D", (G, M_max, N), torch.bfloat16, dev)
+    _dev(masked_m, "masked_m", (G,), torch.int32, dev)
+    _call(fn, dev, _ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(D), _ptr(masked_m), G, M_max, N, K, _stream(A))
     return D
 
 
@@ -219,10 +232,10 @@ def _fused_outputs(lead, I, M, dev, Q, sq, act, with_act):
         sq = torch.empty(lead + (I // 128, M), dtype=torch.float32, device=dev)
     if act is None and with_act:
         act = torch.empty(lead + (M, I), dtype=torch.float32, device=dev)
-    _fp8(Q, "Q", lead + (M, I))
-    _dev(sq, "sq", lead + (I // 128, M), torch.float32)
+    _fp8(Q, "Q", lead + (M, I), dev)
+    _dev(sq, "sq", lead + (I // 128, M), torch.float32, dev)
     if act is not None:
-        _dev(act, "act", lead + (M, I), torch.float32)
+        _dev(act, "act", lead + (M, I), torch.float32, dev)
     return Q, sq, act
 
 
@@ -238,16 +251,16 @@ def gemm_fp8_nt_swiglu_quant(A, sa, B, sb, Q=None, sq=None, act=None, pow2=False
     torch = _torch()
     M, K = A.shape
     N = B.shape[0]
+    dev = A.device
     _fp8(A, "A", (M, K))
-    _fp8(B, "B", (N, K))
+    _fp8(B, "B", (N, K), dev)
     if K % 128 or N % 256:
         raise ValueError("K must be a multiple of 128 and N of 256")
-    _dev(sa, "sa", (K // 128, M), torch.float32)
-    _dev(sb, "sb", (N // 128, K // 128), torch.float32)
-    Q, sq, act = _fused_outputs((), N // 2, M, A.device, Q, sq, act, with_act)
-    _check(lib().fg_gemm_fp8_nt_swiglu_quant(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(Q), _ptr(sq),
-                                             _opt_ptr(act), M, N, K, int(bool(pow2)), _stream(A)),
-           "fg_gemm_fp8_nt_swiglu_quant")
+    _dev(sa, "sa", (K // 128, M), torch.float32, dev)
+    _dev(sb, "sb", (N // 128, K // 128), torch.float32, dev)
+    Q, sq, act = _fused_outputs((), N // 2, M, dev, Q, sq, act, with_act)
+    _call("fg_gemm_fp8_nt_swiglu_quant", dev, _ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(Q), _ptr(sq),
+          _opt_ptr(act), M, N, K, int(bool(pow2)), _stream(A))
     return Q, sq, act
 
 
@@ -258,18 +271,17 @@ def grouped_contiguous_swiglu_quant(A, sa, B, sb, m_indices, Q=None, sq=None, ac
     torch = _torch()
     M, K = A.shape
     G, N = B.shape[0], B.shape[1]
+    dev = A.device
     _fp8(A, "A", (M, K))
-    _fp8(B, "B", (G, N, K))
+    _fp8(B, "B", (G, N, K), dev)
     if K % 128 or N % 256:
         raise ValueError("K must be a multiple of 128 and N of 256")
-    _dev(sa, "sa", (K // 128, M), torch.float32)
-    _dev(sb, "sb", (G, N // 128, K // 128), torch.float32)
-    _dev(m_indices, "m_indices", (M,), torch.int32)
-    Q, sq, act = _fused_outputs((), N // 2, M, A.device, Q, sq, act, with_act)
-    _check(lib().fg_grouped_contiguous_swiglu_quant(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(Q), _ptr(sq),
-                                                    _opt_ptr(act), _ptr(m_indices), M, N, K, G,
-                                                    int(bool(pow2)), _stream(A)),
-           "fg_grouped_contiguous_swiglu_quant")
+    _dev(sa, "sa", (K // 128, M), torch.float32, dev)
+    _dev(sb, "sb", (G, N // 128, K // 128), torch.float32, dev)
+    _dev(m_indices, "m_indices", (M,), torch.int32, dev)
+    Q, sq, act = _fused_outputs((), N // 2, M, dev, Q, sq, act, with_act)
+    _call("fg_grouped_contiguous_swiglu_quant", dev, _ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(Q), _ptr(sq),
+          _opt_ptr(act), _ptr(m_indices), M, N, K, G, int(bool(pow2)), _stream(A))
     return Q, sq, act
 
 
@@ -281,18 +293,17 @@ def grouped_masked_swiglu_quant(A, sa, B, sb, masked_m, Q=None, sq=None, act=Non
     torch = _torch()
     G, M_max, K = A.shape
     N = B.shape[1]
+    dev = A.device
     _fp8(A, "A", (G, M_max, K))
-    _fp8(B, "B", (G, N, K))
+    _fp8(B, "B", (G, N, K), dev)
     if K % 128 or N % 256:
         raise ValueError("K must be a multiple of 128 and N of 256")
-    _dev(sa, "sa", (G, K // 128, M_max), torch.float32)
-    _dev(sb, "sb", (G, N // 128, K // 128), torch.float32)
-    _dev(masked_m, "masked_m", (G,), torch.int32)
-    Q, sq, act = _fused_outputs((G,), N // 2, M_max, A.device, Q, sq, act, with_act)
-    _check(lib().fg_grouped_masked_swiglu_quant(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(Q), _ptr(sq),
-                                                _opt_ptr(act), _ptr(masked_m), G, M_max, N, K,
-                                                int(bool(pow2)), _stream(A)),
-           "fg_grouped_masked_swiglu_quant")
+    _dev(sa, "sa", (G, K // 128, M_max), torch.float32, dev)
+    _dev(sb, "sb", (G, N // 128, K // 128), torch.float32, dev)
+    _dev(masked_m, "masked_m", (G,), torch.int32, dev)
+    Q, sq, act = _fused_outputs((G,), N // 2, M_max, dev, Q, sq, act, with_act)
+    _call("fg_grouped_masked_swiglu_quant", dev, _ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(Q), _ptr(sq),
+          _opt_ptr(act), _ptr(masked_m), G, M_max, N, K, int(bool(pow2)), _stream(A))
     return Q, sq, act
 
 
@@ -337,9 +348,9 @@ def _quant_act(fn, x, q, sa):
     sa_shape = (batch, K // 128, M) if x.dim() == 3 else (K // 128, M)
     if sa is None:
         sa = torch.empty(sa_shape, dtype=torch.float32, device=x.device)
-    _fp8(q, "q", tuple(x.shape))
-    _dev(sa, "sa", sa_shape, torch.float32)
-    _check(getattr(lib(), fn)(_ptr(x), _ptr(q), _ptr(sa), batch, M, K, _stream(x)), fn)
+    _fp8(q, "q", tuple(x.shape), x.device)
+    _dev(sa, "sa", sa_shape, torch.float32, x.device)
+    _call(fn, x.device, _ptr(x), _ptr(q), _ptr(sa), batch, M, K, _stream(x))
     return q, sa
 
 
@@ -369,7 +380,7 @@ def _quant_weight(fn, w, q, sb):
         q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
     if sb is None:
         sb = torch.empty(sb_shape, dtype=torch.float32, device=w.device)
-    _fp8(q, "q", tuple(w.shape))
-    _dev(sb, "sb", sb_shape, torch.float32)
-    _check(getattr(lib(), fn)(_ptr(w), _ptr(q), _ptr(sb), G, N, K, _stream(w)), fn)
+    _fp8(q, "q", tuple(w.shape), w.device)
+    _dev(sb, "sb", sb_shape, torch.float32, w.device)
+    _call(fn, w.device, _ptr(w), _ptr(q), _ptr(sb), G, N, K, _stream(w))
     return q, sb
