@@ -469,9 +469,6 @@ __device__ __forceinline__ void swiglu_quant_epilogue(const Params& p, const f32
   }
 }
 
-// One BM x BN output tile of expert g (dense: g = 0) whose first row is m0
-// and first column n0; rows_valid bounds the rows that have an output. The
-// tile sums K-blocks [kb0, kb0 + nkb) (nkb = 0: all of them, K / 128).
 // Column order of the B tile for the direct-store epilogue. The matrix core
 // gives lane (lr, lq) of a 16x16 sub-tile four consecutive columns 4lq..4lq+3;
 // loading the 32 weight rows of two neighbouring sub-tiles in the order
@@ -1050,7 +1047,9 @@ __device__ __forceinline__ void gemm_tiles(const Params& p, lds_u8* const lds, N
   }
 }
 
-// A single tile (see gemm_tiles).
+// One BM x BN output tile of expert g (dense: g = 0) whose first row is m0
+// and first column n0; rows_valid bounds the rows that have an output (see
+// gemm_tiles).
 template <int LAYOUT, class T, bool POW2, int EPI>
 __device__ __forceinline__ void gemm_tile(const Params& p, lds_u8* const lds, int g, const int m0,
                                           const int n0, const int rows_valid, const int kb0 = 0,
