@@ -41,8 +41,12 @@
  *   - Calls are asynchronous on `stream` (0 = null stream), never synchronise
  *     and never read device data on the host, so they can be captured in a
  *     HIP graph. Rows the call has no output for are never written.
- *   - A fixed device, shape and tile configuration gives bitwise identical
- *     results on every call (no atomics, no split-K).
+ *   - Kernels run on the current device (hipGetDevice); `stream` and every
+ *     pointer must belong to it.
+ *   - Results are bitwise reproducible (no atomics, no split-K), and do not
+ *     depend on the tile configuration or the layout either: every output
+ *     element takes the same K-block dot products and the same FP32
+ *     promotion sequence whichever tile, kernel or layout computes it.
  *   - Return value: FG_OK or a negative FG_E* code; no exception crosses the
  *     ABI. fg_strerror() gives a static description.
  */
