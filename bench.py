@@ -45,7 +45,8 @@ memory traffic (random and all-zero E4M3 codes), and roofline
 `hbm_read_ceiling` is what a plain streaming read (16-byte nontemporal loads,
 the best of three shapes of workgroups and loads in flight) pulls from HBM on
 this device, and each HBM-bound workload's `frac_of_measured_hbm_read` its
-algorithmic bytes per second against that.
+algorithmic bytes per second against that. `device` names the device the line
+was measured on (architecture, compute units, HBM and L2 sizes).
 """
 import argparse
 import ctypes
@@ -477,6 +478,14 @@ def hbm_read_ceiling(torch, warmup_ms, mb=1024):
     return best
 
 
+def device_info(torch):
+    """What the numbers were measured on: the current device's name,
+    architecture, compute units, HBM and L2 sizes."""
+    pr = torch.cuda.get_device_properties(torch.cuda.current_device())
+    return {"name": pr.name, "arch": pr.gcnArchName, "compute_units": pr.multi_processor_count,
+            "hbm_gib": round(pr.total_memory / 2 ** 30, 1), "l2_bytes": pr.L2_cache_size}
+
+
 def kernel_source_hash():
     """Hash of what defines the kernels: the kernel template with comments and
     whitespace removed, and the tile-configuration lines that instantiate it.
@@ -708,6 +717,7 @@ def main():
                    "out": "bf16", "tile": hs["tile"], "input_copies": hs["input_copies"],
                    "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2)},
         "roofline": roof,
+        "device": device_info(torch),
         "mfma_ceiling": ceiling,
         "hbm_read_ceiling": hbm_ceiling,
         "cpu_baseline": cpu_cfg.get(args.workload),
