@@ -275,3 +275,37 @@ def test_grouped_ragged_n(pow2):
     ref, valid = oracle.ref_masked(A, sa, B, sb, mm)
     r = oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
     assert r["ok"], r
+
+
+@pytest.mark.parametrize("pow2", [False, True], ids=["fp32_scales", "pow2_scales"])
+def test_masked_many_experts(pow2):
+    """96 experts (many more groups than tiles per group), small M_max, ragged
+    N, empty and full experts."""
+    G, M_max, N, K = 96, 40, 264, 384
+    print(f"masked many experts G={G} pow2={pow2}", flush=True)
+    A, sa, B, sb, mm = make_masked(G, M_max, N, K, 90, pow2=pow2)
+    mm = mm.copy()
+    mm[:3] = [0, M_max, 1]
+    Ad, sad, Bd, sbd = masked_inputs(A, sa, B, sb)
+    D = new_out((G, M_max, N))
+    (fg.grouped_masked_pow2 if pow2 else fg.grouped_masked)(Ad, sad, Bd, sbd, D, to_dev(mm))
+    torch.cuda.synchronize()
+    ref, valid = oracle.ref_masked(A, sa, B, sb, mm)
+    r = oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("pow2", [False, True], ids=["fp32_scales", "pow2_scales"])
+def test_contiguous_many_experts(pow2):
+    """48 experts of 1..200 rows each (one or two 128-row blocks apiece: many
+    short and odd runs) on the automatic choice."""
+    G, N, K = 48, 256, 256
+    print(f"contiguous many experts G={G} pow2={pow2}", flush=True)
+    A, sa, B, sb, mi = make_contiguous(G, N, K, 91, pow2=pow2, m_lo=1, m_hi=200)
+    Ad, sad, Bd, sbd = dense_inputs(A, sa, B, sb)
+    D = new_out((A.shape[0], N))
+    (fg.grouped_contiguous_pow2 if pow2 else fg.grouped_contiguous)(Ad, sad, Bd, sbd, D, to_dev(mi))
+    torch.cuda.synchronize()
+    ref, valid = oracle.ref_contiguous(A, sa, B, sb, mi)
+    r = oracle.check(d_bits(D), ref, valid, prefill_bits=SENTINEL)
+    assert r["ok"], r
