@@ -372,10 +372,10 @@ def oracle_threads():
 def cpu_baseline(name, target_s):
     """The oracle as it stands (dequantise to fp64 + one fp64 numpy GEMM per
     expert), timed on this host with time.perf_counter: repeated calls until
-    target_s seconds (at least one call, at most 50)."""
+    target_s seconds (at least one call, at most 500)."""
     call, flop, desc = oracle_case(name)
     reps, spent = 0, 0.0
-    while reps == 0 or (spent < target_s and reps < 50):
+    while reps == 0 or (spent < target_s and reps < 500):
         t0 = time.perf_counter()
         call()
         spent += time.perf_counter() - t0
